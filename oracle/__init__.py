@@ -1,0 +1,191 @@
+"""CPU oracle for the WeDLM streaming-decode step -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg import this package.  The product library never does.
+The arithmetic lives in ``wedlm_oracle.c`` (plain C + OpenMP, float64);
+this module only marshals numpy arrays to it.
+
+Every function is pinned by the CPU test suite (tests/test_oracle_*.py)
+against closed forms, brute force on tiny inputs and the invariants the
+pages fix; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+F32, BF16, F64 = 0, 1, 2
+_DT = {"f32": F32, "bf16": BF16, "f64": F64}
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB) or (
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
+            _build.build()
+        lib = C.CDLL(_build.LIB)
+        P = C.c_void_p
+        i32, i64, f64 = C.c_int, C.c_int64, C.c_double
+        lib.wo_num_threads.restype = i32
+        lib.wo_round_storage.argtypes = [f64, i32]
+        lib.wo_round_storage.restype = f64
+        lib.wo_reorder_perm.argtypes = [i32, P, P]
+        lib.wo_reorder_perm.restype = i32
+        lib.wo_rope.argtypes = [i32, f64, C.c_int32, P, P]
+        lib.wo_rope.restype = None
+        lib.wo_reorder.argtypes = [i32, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, P, P]
+        lib.wo_reorder.restype = i32
+        lib.wo_attention.argtypes = [i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, i64, P, P]
+        lib.wo_attention.restype = None
+        lib.wo_row_stats.argtypes = [i32, P, P, P]
+        lib.wo_row_stats.restype = None
+        lib.wo_vocab_stats.argtypes = [i64, i32, P, P, P]
+        lib.wo_vocab_stats.restype = None
+        lib.wo_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                         f64, f64, C.c_int32, P]
+        lib.wo_select_commit.restype = i32
+        _LIB = lib
+    return _LIB
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(_lib().wo_num_threads())
+
+
+def round_storage(x: float, dtype: str) -> float:
+    return float(_lib().wo_round_storage(float(x), _DT[dtype]))
+
+
+def reorder_perm(filled: np.ndarray) -> np.ndarray:
+    """Physical row -> logical slot, per sequence.  filled: [B, W] or [W]."""
+    f = _c(np.atleast_2d(filled), np.uint8)
+    B, W = f.shape
+    perm = np.empty((B, W), dtype=np.int32)
+    for b in range(B):
+        _lib().wo_reorder_perm(W, _p(f[b]), _p(perm[b]))
+    return perm if np.ndim(filled) == 2 else perm[0]
+
+
+def rope(x: np.ndarray, p: int, base: float) -> np.ndarray:
+    x = _c(x, np.float64)
+    y = np.empty_like(x)
+    _lib().wo_rope(x.shape[-1], float(base), int(p), _p(x), _p(y))
+    return y
+
+
+def reorder(filled, pos, q, k, v, dtype: str, base: float):
+    """q/k/v as float64 values [B, W, H, D] (logical order, before RoPE).
+    Returns perm [B,W], q_phys [B,W,Hq,D], k_win/v_win [B,W,Hkv,D] (physical)."""
+    q = _c(q, np.float64); k = _c(k, np.float64); v = _c(v, np.float64)
+    filled = _c(filled, np.uint8); pos = _c(pos, np.int32)
+    B, W, Hq, D = q.shape
+    Hkv = k.shape[2]
+    perm = np.empty((B, W), dtype=np.int32)
+    qp = np.empty_like(q)
+    kw = np.empty_like(k)
+    vw = np.empty_like(v)
+    rc = _lib().wo_reorder(B, W, Hq, Hkv, D, _DT[dtype], float(base), _p(filled), _p(pos),
+                           _p(q), _p(k), _p(v), _p(perm), _p(qp), _p(kw), _p(vw))
+    if rc != 0:
+        raise ValueError("positions must be strictly increasing within each window")
+    return perm, qp, kw, vw
+
+
+def attention(q_phys, dense_k: Sequence[np.ndarray], dense_v: Sequence[np.ndarray],
+              ctx_len, perm, scale: Optional[float] = None, rows=None):
+    """Windowed causal GQA attention.  q_phys [B,W,Hq,D] float64 (physical
+    order); dense_k/v[b] [L_b + W, Hkv, D] float64 (logical token order).
+    rows: optional int array [n, 3] of (b, r, h); only those outputs are
+    computed (others stay NaN).  Returns out [B, W, Hq, D] in logical slot
+    order."""
+    q_phys = _c(q_phys, np.float64)
+    B, W, Hq, D = q_phys.shape
+    Hkv = dense_k[0].shape[1]
+    ctx_len = _c(ctx_len, np.int32)
+    perm = _c(perm, np.int32)
+    for b in range(B):
+        assert dense_k[b].shape[0] == int(ctx_len[b]) + W, "dense cache must hold L_b + W tokens"
+    K = _c(np.concatenate([np.asarray(x, np.float64) for x in dense_k], axis=0), np.float64)
+    V = _c(np.concatenate([np.asarray(x, np.float64) for x in dense_v], axis=0), np.float64)
+    off = np.zeros(B, dtype=np.int64)
+    off[1:] = np.cumsum([x.shape[0] for x in dense_k])[:-1]
+    out = np.full((B, W, Hq, D), np.nan, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        n, rp = 0, None
+    else:
+        rows = _c(rows, np.int32).reshape(-1, 3)
+        n, rp = rows.shape[0], rows
+    _lib().wo_attention(B, W, Hq, Hkv, D, float(scale), _p(q_phys), _p(K), _p(V), _p(off),
+                        _p(ctx_len), _p(perm), n, _p(rp), _p(out))
+    return out
+
+
+def row_stats(z: np.ndarray):
+    """(argmax, entropy in nats) of each row of z [..., V] (fp32 input)."""
+    z = _c(z, np.float32)
+    V = z.shape[-1]
+    R = z.size // V
+    am = np.empty(R, dtype=np.int32)
+    H = np.empty(R, dtype=np.float64)
+    _lib().wo_vocab_stats(R, V, _p(z), _p(am), _p(H))
+    return am.reshape(z.shape[:-1]), H.reshape(z.shape[:-1])
+
+
+def select_commit(logits: np.ndarray, tok, filled, pos, ctx_len, alpha: float, tau: float,
+                  mask_id: int, row_index: Optional[np.ndarray] = None):
+    """One commit / Eq. 11 select / refill step.  Window state arrays are
+    copied; returns a dict with the new state and the step's outputs."""
+    tok = np.array(tok, dtype=np.int32, copy=True)
+    filled = np.array(filled, dtype=np.uint8, copy=True)
+    pos = np.array(pos, dtype=np.int32, copy=True)
+    ctx = np.array(ctx_len, dtype=np.int32, copy=True)
+    B, W = tok.shape
+    logits = _c(logits, np.float32)
+    V = logits.shape[-1]
+    ri = None if row_index is None else _c(row_index, np.int64)
+    n_commit = np.empty(B, dtype=np.int32)
+    committed = np.empty((B, W), dtype=np.int32)
+    am = np.empty((B, W), dtype=np.int32)
+    ent = np.empty((B, W), dtype=np.float32)
+    margin = np.empty(B, dtype=np.float64)
+    rc = _lib().wo_select_commit(B, W, V, _p(logits), _p(ri), _p(tok), _p(filled), _p(pos),
+                                 _p(ctx), _p(n_commit), _p(committed), _p(am), _p(ent),
+                                 float(alpha), float(tau), int(mask_id), _p(margin))
+    if rc != 0:
+        raise ValueError("a masked slot's logits row was not supplied")
+    return dict(tok=tok, filled=filled, pos=pos, ctx_len=ctx, n_commit=n_commit,
+                committed=committed, argmax=am, entropy=ent, margin=margin)
+
+
+def decode_step_attention(inp, scale: Optional[float] = None, rows=None):
+    """Oracle for reorder + attention on one batch drawn by
+    workloads.make_attn_inputs.  Returns a dict
+    with perm, q_phys, k_win, v_win (physical order, storage-rounded) and out
+    (logical slot order)."""
+    from workloads import storage_to_f64
+    cfg = inp.cfg
+    dt = cfg.dtype
+    perm, qp, kw, vw = reorder(inp.filled, inp.pos, storage_to_f64(inp.q, dt),
+                               storage_to_f64(inp.k, dt), storage_to_f64(inp.v, dt),
+                               dt, cfg.rope_base)
+    dk = [np.concatenate([storage_to_f64(inp.prefix_k[b], dt), kw[b]], axis=0) for b in range(cfg.B)]
+    dv = [np.concatenate([storage_to_f64(inp.prefix_v[b], dt), vw[b]], axis=0) for b in range(cfg.B)]
+    out = attention(qp, dk, dv, inp.ctx_len, perm, scale=scale, rows=rows)
+    return dict(perm=perm, q_phys=qp, k_win=kw, v_win=vw, out=out)
