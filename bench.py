@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the WeDLM streaming-decode step on one MI355X.
+
+A step is one pass of the whole decode path over one batch: wedlm_reorder
+(Topological Reordering + logical RoPE + KV append), wedlm_step_attn
+(windowed causal GQA attention over the paged prefix cache) and
+wedlm_select_commit (vocabulary confidence, commit, Eq. 11 fill, refill).
+Steps stream: each one commits tokens, so the context grows as it would in
+decoding.  Inputs are synthetic and resident in HBM before timing starts.
+
+Default workload: batch 4, 32 Q / 8 KV heads, head dim 128, 32768 cached
+tokens in 16-token pages (shuffled), window 32 (16 observed), bf16; logits
+[4, 32, 151936] fp32 drawn with the low/high-entropy mixture.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints one JSON line (rank 0).  The attention call is timed with HIP events
+on the stream it runs on; its algorithmic bytes (K/V of every visible key,
+read once, plus Q in and O out) per launch are divided by that time.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "window tokens/sec and decode steps/sec per GPU; attn achieved HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_b4",
+                    choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32"])
+    ap.add_argument("--vocab", type=int, default=151936)
+    ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
+    ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = auto)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding paragraph of DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    import causal_attention_diffusion_amd as wd
+
+    dev = torch.device("cuda:0")
+    cfg = wl.CONFIGS[args.workload]
+    scfg = wl.SelectConfig("bench", B=cfg.B, W=cfg.W, V=args.vocab, seed=1005, alpha=0.25, tau=9.0,
+                           steps=0, kind="mixture")
+    total_steps = args.steps + args.warmup
+    spare = total_steps * cfg.W + cfg.W
+    inp = wl.make_attn_inputs(cfg, spare_tokens=spare)
+    t = wl.device_attn_inputs(inp, dev)
+    wd.wedlm_set_attn_split_keys(args.split_keys)
+
+    B, W = cfg.B, cfg.W
+    mask_id = args.vocab
+    # window state as produced by the previous step: flags from the workload, tokens filled
+    tok0 = np.where(inp.filled == 1, (np.arange(B * W).reshape(B, W) * 7919) % args.vocab,
+                    mask_id).astype(np.int32)
+    tok = torch.from_numpy(tok0).to(dev)
+    filled, pos, ctx = t["filled"], t["pos"], t["ctx_len"]
+    max_ctx = int(inp.ctx_len.max()) + total_steps * W
+    ws_attn = wd.attn_workspace_tensor(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
+    ws_sel = wd.select_workspace_tensor(B, W, args.vocab, dev)
+    logits = [wl.make_logits_torch(scfg, i, dev) for i in range(args.logit_ring)]
+    n_commit_hist = torch.zeros((total_steps, B), dtype=torch.int32, device=dev)
+    committed = torch.empty((B, W), dtype=torch.int32, device=dev)
+    argmax_hist = torch.empty((total_steps, B, W), dtype=torch.int32, device=dev)  # -1 on unmasked slots
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(total_steps)]
+    ev_sel = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(total_steps)]
+    nsplit, split_keys = wd.wedlm_attn_plan(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
+
+    def step(i):
+        wd.wedlm_reorder(filled, pos, t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"], t["v_cache"],
+                         t["block_table"], ctx, t["perm"], cfg.rope_base, dev_status=t["status"])
+        ev[i][0].record()
+        wd.wedlm_step_attn(t["q_phys"], t["k_cache"], t["v_cache"], t["block_table"], ctx, t["perm"],
+                           t["out"], max_ctx_len=max_ctx, workspace=ws_attn, dev_status=t["status"])
+        ev[i][1].record()
+        ev_sel[i][0].record()
+        wd.wedlm_select_commit(logits[i % len(logits)], tok, filled, pos, ctx, n_commit_hist[i], committed,
+                               scfg.alpha, scfg.tau, mask_id, ws_sel, argmax_out=argmax_hist[i])
+        ev_sel[i][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ctx_start = ctx.cpu().numpy().astype(np.int64)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    status = int(t["status"].item())
+    if status != 0:
+        print(f"device status {status} (bad ctx/page/perm)", file=sys.stderr)
+        sys.exit(3)
+    K = args.steps
+    ms_step = elapsed * 1e3 / K
+    attn_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)])
+    sel_ms = np.array([ev_sel[i][0].elapsed_time(ev_sel[i][1]) for i in range(args.warmup, total_steps)])
+    nc = n_commit_hist.cpu().numpy().astype(np.int64)[args.warmup:]
+    # per-launch algorithmic bytes of the attention call
+    Hkv, Hq, D = cfg.Hkv, cfg.Hq, cfg.D
+    eb = 2 if cfg.dtype == "bf16" else 4
+    L_steps = ctx_start[None, :] + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(nc, 0)[:-1]], 0)
+    kv_bytes = ((L_steps + W) * Hkv * D * 2 * eb).sum(1)                # K and V of every visible key
+    qo_bytes = 2 * B * W * Hq * D * eb                                   # Q in, O out
+    attn_bytes = kv_bytes + qo_bytes
+    attn_gbs = float((attn_bytes / (attn_ms * 1e-3)).mean() / 1e9)
+    mean_attn_bytes = float(attn_bytes.mean())
+    attn_avg_ms = float(attn_ms.mean())
+    achieved = mean_attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    tokens_per_s = B * W / (ms_step * 1e-3)
+    masked_rows = (argmax_hist[args.warmup:] >= 0).sum(dim=(1, 2)).cpu().numpy()
+    sel_bytes = masked_rows * args.vocab * 4                              # logits rows actually read
+    sel_gbs = float((sel_bytes / (sel_ms * 1e-3)).mean() / 1e9)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "window tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} W={W} Hq={Hq} Hkv={Hkv} D={D} "
+                               f"prefix={int(inp.ctx_len.max()) if cfg.L_range is None else str(cfg.L_range)} "
+                               f"page=16 vocab={args.vocab} streaming decode step (reorder+attn+select/commit)",
+                   "batch": B, "window": W, "prefix_tokens_at_start": int(ctx_start.max()),
+                   "vocab": args.vocab, "split_kv": [nsplit, split_keys]},
+        "steps_per_s": round(1e3 / ms_step, 2),
+        "attn": {"avg_ms": round(attn_avg_ms, 5), "alg_bytes_per_launch": int(mean_attn_bytes),
+                 "GB_per_s": round(achieved, 1)},
+        "select_commit": {"avg_ms": round(float(sel_ms.mean()), 5), "masked_rows_per_step": float(masked_rows.mean()),
+                          "GB_per_s": round(sel_gbs, 1)},
+        "reorder_plus_gaps_ms": round(ms_step - attn_avg_ms - float(sel_ms.mean()), 5),
+        "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "wedlm_step_attn (attn_split + attn_combine)"},
+    }
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, args, inp)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, args, inp):
+    """The oracle, untuned, on the host cores: one whole decode step (reorder,
+    attention of every row, select/commit over the full vocabulary) for a
+    sample of the batch's sequences, reported in window tokens/s."""
+    import oracle
+    import workloads as wl
+    nseq = args.cpu_seqs or cfg.B
+    sel = list(range(nseq))
+    dt = cfg.dtype
+    q = wl.storage_to_f64(inp.q[sel], dt)
+    k = wl.storage_to_f64(inp.k[sel], dt)
+    v = wl.storage_to_f64(inp.v[sel], dt)
+    pk = [wl.storage_to_f64(inp.prefix_k[b], dt) for b in sel]
+    pv = [wl.storage_to_f64(inp.prefix_v[b], dt) for b in sel]
+    scfg = wl.SelectConfig("cpu", B=nseq, W=cfg.W, V=args.vocab, seed=1005, alpha=0.25, tau=9.0,
+                           steps=0, kind="mixture")
+    lg = wl.make_logits_np(scfg, 0)
+    tok = np.where(inp.filled[sel] == 1, 1, args.vocab).astype(np.int32)
+    t0 = time.perf_counter()
+    perm, qp, kw, vw = oracle.reorder(inp.filled[sel], inp.pos[sel], q, k, v, dt, cfg.rope_base)
+    dk = [np.concatenate([pk[i], kw[i]], 0) for i in range(nseq)]
+    dv = [np.concatenate([pv[i], vw[i]], 0) for i in range(nseq)]
+    oracle.attention(qp, dk, dv, inp.ctx_len[sel], perm)
+    oracle.select_commit(lg, tok, inp.filled[sel], inp.pos[sel], inp.ctx_len[sel], 0.25, 9.0, args.vocab)
+    dt_s = time.perf_counter() - t0
+    return {"value": round(nseq * cfg.W / dt_s, 3), "unit": "window tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{nseq} of {cfg.B} sequences, one full step (reorder, all {cfg.W * cfg.Hq} "
+                      f"attention rows per sequence, select/commit over V={args.vocab}); {dt_s:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

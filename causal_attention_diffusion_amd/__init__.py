@@ -1,0 +1,35 @@
+"""WeDLM streaming-decode step on MI355X (gfx950).
+
+Python binding of ``libwedlm.so`` (see ``include/wedlm.h``).  The functions
+carry the C names and only marshal torch tensors to device pointers; every
+step of the decode path runs in the HIP kernels.  There is no CPU fallback:
+if the library is not built, every call raises.
+
+    import causal_attention_diffusion_amd as wd
+    wd.wedlm_reorder(filled, pos, q, k, v, q_phys, k_cache, v_cache,
+                     block_table, ctx_len, perm, rope_base)
+    wd.wedlm_step_attn(q_phys, k_cache, v_cache, block_table, ctx_len, perm,
+                       out, max_ctx_len=..., workspace=ws)
+    wd.wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit,
+                           committed, alpha=..., tau=..., mask_id=..., workspace=ws2)
+"""
+from .binding import (  # noqa: F401
+    WEDLM_BF16,
+    WEDLM_F32,
+    WedlmError,
+    attn_plan,
+    lib_path,
+    load_library,
+    make_shape,
+    select_workspace_tensor,
+    attn_workspace_tensor,
+    wedlm_attn_plan,
+    wedlm_last_error,
+    wedlm_reorder,
+    wedlm_select_commit,
+    wedlm_select_commit_workspace,
+    wedlm_set_attn_split_keys,
+    wedlm_step_attn,
+    wedlm_step_attn_workspace,
+    wedlm_version,
+)

@@ -1,0 +1,238 @@
+"""ctypes binding of libwedlm.so: argument marshalling only.
+
+Shapes are read off the torch tensors, pointers and the current HIP stream
+are passed to the C entry points of ``include/wedlm.h``.  A non-OK status
+raises WedlmError with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libwedlm.so")
+_LIB = None
+
+WEDLM_F32, WEDLM_BF16 = 0, 1
+PAGE = 16
+
+
+class WedlmError(RuntimeError):
+    pass
+
+
+class WedlmShape(C.Structure):
+    _fields_ = [("B", C.c_int32), ("W", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32),
+                ("D", C.c_int32), ("page_size", C.c_int32), ("max_pages", C.c_int32),
+                ("num_pages", C.c_int32), ("dtype", C.c_int32)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libwedlm.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise WedlmError(f"{_LIB_PATH} is not built; run `python -m causal_attention_diffusion_amd.build` "
+                         "(there is no fallback path)")
+    lib = C.CDLL(_LIB_PATH)
+    P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    S = C.POINTER(WedlmShape)
+    lib.wedlm_reorder.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, C.c_double, P, P]
+    lib.wedlm_reorder.restype = C.c_int
+    lib.wedlm_step_attn_workspace.argtypes = [S, i32]
+    lib.wedlm_step_attn_workspace.restype = sz
+    lib.wedlm_step_attn.argtypes = [S, P, P, P, P, P, P, P, C.c_float, i32, P, sz, P, P]
+    lib.wedlm_step_attn.restype = C.c_int
+    lib.wedlm_select_commit_workspace.argtypes = [i32, i32, i32]
+    lib.wedlm_select_commit_workspace.restype = sz
+    lib.wedlm_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P,
+                                        C.c_float, C.c_float, i32, P, sz, P]
+    lib.wedlm_select_commit.restype = C.c_int
+    lib.wedlm_attn_plan.argtypes = [S, i32, C.POINTER(i32), C.POINTER(i32)]
+    lib.wedlm_attn_plan.restype = C.c_int
+    lib.wedlm_set_attn_split_keys.argtypes = [i32]
+    lib.wedlm_set_attn_split_keys.restype = C.c_int
+    lib.wedlm_last_error.restype = C.c_char_p
+    lib.wedlm_version.restype = C.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise WedlmError(f"status {rc}: {load_library().wedlm_last_error().decode()}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise WedlmError("tensors must be contiguous")
+    if t.device.type != "cuda":
+        raise WedlmError("tensors must be on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return WEDLM_F32
+    if t.dtype == torch.bfloat16:
+        return WEDLM_BF16
+    raise WedlmError(f"dtype {t.dtype} not supported (float32, bfloat16)")
+
+
+def make_shape(B, W, Hq, Hkv, D, max_pages, num_pages, dtype) -> WedlmShape:
+    return WedlmShape(B, W, Hq, Hkv, D, PAGE, max_pages, num_pages, dtype)
+
+
+def _shape_from(q, k_cache, block_table) -> WedlmShape:
+    if q.dim() != 4 or k_cache.dim() != 4 or block_table.dim() != 2:
+        raise WedlmError("expected q [B,W,Hq,D], cache [pages,Hkv,16,D], block_table [B,max_pages]")
+    B, W, Hq, D = q.shape
+    P, Hkv, page, D2 = k_cache.shape
+    if page != PAGE or D2 != D:
+        raise WedlmError(f"cache must be [pages, Hkv, {PAGE}, {D}], got {tuple(k_cache.shape)}")
+    if block_table.shape[0] != B:
+        raise WedlmError("block_table must be [B, max_pages]")
+    return make_shape(B, W, Hq, Hkv, D, block_table.shape[1], P, _dtype_code(q))
+
+
+def _expect(t, name, shape, dtype):
+    """Shape/dtype check of one argument before its pointer reaches a kernel."""
+    if t is None:
+        raise WedlmError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise WedlmError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def _opt(t, name, shape, dtype):
+    if t is not None:
+        _expect(t, name, shape, dtype)
+
+
+# ---------------------------------------------------------------- entry points
+def wedlm_reorder(filled, pos, q, k, v, q_phys, k_cache, v_cache, block_table, ctx_len, perm,
+                  rope_base: float, dev_status=None, stream=None):
+    import torch
+    s = _shape_from(q, k_cache, block_table)
+    B, W, Hkv, D = s.B, s.W, s.Hkv, s.D
+    _expect(filled, "filled", (B, W), torch.uint8)
+    _expect(pos, "pos", (B, W), torch.int32)
+    _expect(k, "k", (B, W, Hkv, D), q.dtype)
+    _expect(v, "v", (B, W, Hkv, D), q.dtype)
+    _expect(q_phys, "q_phys", tuple(q.shape), q.dtype)
+    _expect(v_cache, "v_cache", tuple(k_cache.shape), q.dtype)
+    _expect(k_cache, "k_cache", tuple(k_cache.shape), q.dtype)
+    _expect(block_table, "block_table", tuple(block_table.shape), torch.int32)
+    _expect(ctx_len, "ctx_len", (B,), torch.int32)
+    _expect(perm, "perm", (B, W), torch.int32)
+    _opt(dev_status, "dev_status", (1,), torch.int32)
+    _check(load_library().wedlm_reorder(
+        C.byref(s), _ptr(filled), _ptr(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(q_phys), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), _ptr(ctx_len), _ptr(perm), float(rope_base),
+        _ptr(dev_status), _stream(stream)))
+
+
+def wedlm_step_attn_workspace(q_phys, k_cache, block_table, max_ctx_len: int) -> int:
+    s = _shape_from(q_phys, k_cache, block_table)
+    return int(load_library().wedlm_step_attn_workspace(C.byref(s), int(max_ctx_len)))
+
+
+def attn_workspace_tensor(q_phys, k_cache, block_table, max_ctx_len: int):
+    import torch
+    n = wedlm_step_attn_workspace(q_phys, k_cache, block_table, max_ctx_len)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q_phys.device)
+
+
+def wedlm_step_attn(q_phys, k_cache, v_cache, block_table, ctx_len, perm, out, max_ctx_len: int,
+                    workspace=None, scale: float = 0.0, dev_status=None, stream=None):
+    import torch
+    s = _shape_from(q_phys, k_cache, block_table)
+    _expect(k_cache, "k_cache", tuple(k_cache.shape), q_phys.dtype)
+    _expect(v_cache, "v_cache", tuple(k_cache.shape), q_phys.dtype)
+    _expect(block_table, "block_table", tuple(block_table.shape), torch.int32)
+    _expect(ctx_len, "ctx_len", (s.B,), torch.int32)
+    _expect(perm, "perm", (s.B, s.W), torch.int32)
+    _expect(out, "out", tuple(q_phys.shape), q_phys.dtype)
+    _opt(dev_status, "dev_status", (1,), torch.int32)
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise WedlmError("workspace must be a uint8 tensor")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load_library().wedlm_step_attn(
+        C.byref(s), _ptr(q_phys), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_len),
+        _ptr(perm), _ptr(out), float(scale), int(max_ctx_len), _ptr(workspace), ws_bytes,
+        _ptr(dev_status), _stream(stream)))
+
+
+def wedlm_attn_plan(q_phys, k_cache, block_table, max_ctx_len: int):
+    s = _shape_from(q_phys, k_cache, block_table)
+    ns, sk = C.c_int32(), C.c_int32()
+    _check(load_library().wedlm_attn_plan(C.byref(s), int(max_ctx_len), C.byref(ns), C.byref(sk)))
+    return ns.value, sk.value
+
+
+def attn_plan(B, W, Hq, Hkv, D, max_pages, num_pages, dtype, max_ctx_len):
+    s = make_shape(B, W, Hq, Hkv, D, max_pages, num_pages, dtype)
+    ns, sk = C.c_int32(), C.c_int32()
+    _check(load_library().wedlm_attn_plan(C.byref(s), int(max_ctx_len), C.byref(ns), C.byref(sk)))
+    return ns.value, sk.value
+
+
+def wedlm_set_attn_split_keys(keys: int):
+    _check(load_library().wedlm_set_attn_split_keys(int(keys)))
+
+
+def wedlm_select_commit_workspace(B: int, W: int, V: int) -> int:
+    return int(load_library().wedlm_select_commit_workspace(int(B), int(W), int(V)))
+
+
+def select_workspace_tensor(B: int, W: int, V: int, device):
+    """Zero-filled workspace for wedlm_select_commit (the calls keep it zeroed)."""
+    import torch
+    return torch.zeros(max(wedlm_select_commit_workspace(B, W, V), 1), dtype=torch.uint8, device=device)
+
+
+def wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit, committed, alpha: float,
+                        tau: float, mask_id: int, workspace, argmax_out=None, entropy_out=None,
+                        stream=None):
+    import torch
+    if logits.dim() != 3 or logits.dtype != torch.float32:
+        raise WedlmError("logits must be a [B, W, V] float32 tensor")
+    B, W, V = logits.shape
+    _expect(tok, "tok", (B, W), torch.int32)
+    _expect(filled, "filled", (B, W), torch.uint8)
+    _expect(pos, "pos", (B, W), torch.int32)
+    _expect(ctx_len, "ctx_len", (B,), torch.int32)
+    _expect(n_commit, "n_commit", (B,), torch.int32)
+    _expect(committed, "committed", (B, W), torch.int32)
+    _opt(argmax_out, "argmax_out", (B, W), torch.int32)
+    _opt(entropy_out, "entropy_out", (B, W), torch.float32)
+    if workspace is None or workspace.dtype != torch.uint8:
+        raise WedlmError("workspace must be a uint8 tensor (select_workspace_tensor)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().wedlm_select_commit(
+        B, W, V, _ptr(logits), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len), _ptr(n_commit),
+        _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), float(alpha), float(tau), int(mask_id),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wedlm_last_error() -> str:
+    return load_library().wedlm_last_error().decode()
+
+
+def wedlm_version() -> str:
+    return load_library().wedlm_version().decode()

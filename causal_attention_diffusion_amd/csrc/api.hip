@@ -1,0 +1,226 @@
+// api.hip -- the extern "C" entry points of libwedlm: argument checks,
+// launch planning and kernel launches.  No call allocates device memory or
+// synchronises the device.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "kernels.hpp"
+
+namespace wedlm {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+static int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+static int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) {
+        g_err[0] = 0;
+        return WEDLM_OK;
+    }
+    return fail(WEDLM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace wedlm
+
+
+using namespace wedlm;
+
+static int check_shape(const wedlm_shape* s) {
+    if (!s) return fail(WEDLM_ERR_ARG, "shape is NULL");
+    if (s->B < 1 || s->W < 1 || s->W > 64)
+        return fail(WEDLM_ERR_SHAPE, "need B >= 1 and 1 <= W <= 64 (B=%d W=%d)", s->B, s->W);
+    if (s->Hq < 1 || s->Hkv < 1 || s->Hq % s->Hkv != 0 || s->Hq / s->Hkv > 16)
+        return fail(WEDLM_ERR_SHAPE, "need Hkv >= 1, Hq %% Hkv == 0 and Hq/Hkv <= 16 (Hq=%d Hkv=%d)", s->Hq, s->Hkv);
+    if (s->D != 64 && s->D != 128) return fail(WEDLM_ERR_UNSUPPORTED, "head dim %d: built for 64 and 128", s->D);
+    if (s->page_size != kPage) return fail(WEDLM_ERR_UNSUPPORTED, "page_size %d: built for 16", s->page_size);
+    if (s->max_pages < 1 || s->num_pages < 1)
+        return fail(WEDLM_ERR_SHAPE, "max_pages (%d) and num_pages (%d) must be >= 1", s->max_pages, s->num_pages);
+    if (s->dtype != WEDLM_F32 && s->dtype != WEDLM_BF16) return fail(WEDLM_ERR_ARG, "dtype %d", s->dtype);
+    // every element offset must fit the kernels' 64-bit arithmetic and the
+    // 32-bit grid: keep the grid below 2^31 work-groups
+    if ((int64_t)s->B * s->W > (1ll << 24)) return fail(WEDLM_ERR_SHAPE, "B*W too large");
+    return WEDLM_OK;
+}
+
+extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const int32_t* pos, const void* q,
+                             const void* k, const void* v, void* q_phys, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* ctx_len, int32_t* perm,
+                             double rope_base, int32_t* dev_status, void* stream) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!filled || !pos || !q || !k || !v || !q_phys || !k_cache || !v_cache || !block_table || !ctx_len || !perm)
+        return fail(WEDLM_ERR_ARG, "wedlm_reorder: NULL device pointer");
+    if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(WEDLM_ERR_ARG, "rope_base must be > 1");
+    ReorderArgs a;
+    a.filled = filled; a.pos = pos; a.q = q; a.k = k; a.v = v; a.q_phys = q_phys;
+    a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table; a.ctx_len = ctx_len;
+    a.perm = perm; a.status = dev_status;
+    a.B = s->B; a.W = s->W; a.Hq = s->Hq; a.Hkv = s->Hkv; a.D = s->D;
+    a.max_pages = s->max_pages; a.num_pages = s->num_pages;
+    a.log2_base = log2(rope_base);
+    return hip_status(launch_reorder(a, s->dtype, (hipStream_t)stream), "wedlm_reorder launch");
+}
+
+// ---------------------------------------------------------------- attention plan
+static int32_t g_split_override = 0;
+
+struct Plan {
+    int nw, chunk, RT, row_tiles, nsplit, split_keys;
+    size_t ws_bytes, off_ml;
+};
+
+static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
+    Plan p;
+    const int G = s->Hq / s->Hkv;
+    const int M = s->W * G;
+    p.nw = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+    p.chunk = attn_chunk(s->dtype, p.nw);
+    p.RT = 32 * p.nw;
+    p.row_tiles = (M + p.RT - 1) / p.RT;
+    const int64_t T = (int64_t)max_ctx_len + s->W;
+    const int64_t pairs = (int64_t)s->B * s->Hkv * p.row_tiles;
+    int64_t sk;
+    if (g_split_override > 0) {
+        sk = g_split_override;
+    } else {
+        // aim at ~2 resident work-groups per CU over 256 CUs, but keep the
+        // fp32 partials (RT*D*4 bytes per split) small next to the KV bytes
+        // a split streams: at least 8 keys per row of the tile, >= 128 keys
+        const int64_t target = 512;
+        sk = (T * pairs + target - 1) / target;
+        int64_t lo = (int64_t)p.RT * 8;
+        if (lo < 128) lo = 128;
+        if (sk < lo) sk = lo;
+    }
+    sk = (sk + p.chunk - 1) / p.chunk * p.chunk;
+    if (sk > (int64_t)kMaxSplitPages * kPage) sk = (int64_t)kMaxSplitPages * kPage;
+    if (sk >= T) sk = (T + p.chunk - 1) / p.chunk * p.chunk;  // one split covers everything
+    p.split_keys = (int)sk;
+    p.nsplit = (int)((T + sk - 1) / sk);
+    if (p.nsplit < 1) p.nsplit = 1;
+    if (p.nsplit == 1) {
+        p.ws_bytes = 0;
+        p.off_ml = 0;
+    } else {
+        const size_t rows = (size_t)pairs * p.nsplit * p.RT;
+        const size_t o_bytes = (rows * s->D * sizeof(float) + 255) / 256 * 256;
+        p.off_ml = o_bytes;
+        p.ws_bytes = o_bytes + (rows * sizeof(float2) + 255) / 256 * 256;
+    }
+    return p;
+}
+
+extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_t* nsplit, int32_t* split_keys) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (max_ctx_len < 0) return fail(WEDLM_ERR_ARG, "max_ctx_len must be >= 0");
+    Plan p = make_plan(s, max_ctx_len);
+    if (nsplit) *nsplit = p.nsplit;
+    if (split_keys) *split_keys = p.split_keys;
+    g_err[0] = 0;
+    return WEDLM_OK;
+}
+
+extern "C" int wedlm_set_attn_split_keys(int32_t keys) {
+    if (keys != 0 && (keys < 64 || keys > kMaxSplitPages * kPage || keys % 64 != 0))
+        return fail(WEDLM_ERR_ARG, "split keys must be 0 or a multiple of 64 in [64, %d]", kMaxSplitPages * kPage);
+    g_split_override = keys;
+    g_err[0] = 0;
+    return WEDLM_OK;
+}
+
+extern "C" size_t wedlm_step_attn_workspace(const wedlm_shape* s, int32_t max_ctx_len) {
+    if (check_shape(s) || max_ctx_len < 0) return 0;
+    return make_plan(s, max_ctx_len).ws_bytes;
+}
+
+extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* ctx_len, const int32_t* perm, void* out,
+                               float scale, int32_t max_ctx_len, void* workspace, size_t ws_bytes,
+                               int32_t* dev_status, void* stream) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!q_phys || !k_cache || !v_cache || !block_table || !ctx_len || !perm || !out)
+        return fail(WEDLM_ERR_ARG, "wedlm_step_attn: NULL device pointer");
+    if (max_ctx_len < 0 || (int64_t)max_ctx_len + s->W > (int64_t)s->max_pages * kPage)
+        return fail(WEDLM_ERR_SHAPE, "max_ctx_len %d + W exceeds max_pages * page_size", max_ctx_len);
+    if (!(scale >= 0.f) || !isfinite(scale)) return fail(WEDLM_ERR_ARG, "scale must be finite and >= 0");
+    Plan p = make_plan(s, max_ctx_len);
+    if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes))
+        return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", p.ws_bytes, workspace ? ws_bytes : 0);
+    AttnArgs a;
+    a.q = q_phys; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
+    a.ctx_len = ctx_len; a.perm = perm; a.out = out;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = p.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.off_ml) : nullptr;
+    a.status = dev_status;
+    a.B = s->B; a.W = s->W; a.Hq = s->Hq; a.Hkv = s->Hkv; a.G = s->Hq / s->Hkv; a.M = s->W * a.G;
+    a.max_pages = s->max_pages; a.num_pages = s->num_pages;
+    a.RT = p.RT; a.row_tiles = p.row_tiles; a.nsplit = p.nsplit; a.split_keys = p.split_keys;
+    a.max_ctx = max_ctx_len;
+    const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)s->D);
+    a.scale_log2 = sc * kLog2e;
+    return hip_status(launch_attn(a, s->dtype, s->D, p.nw, (hipStream_t)stream), "wedlm_step_attn launch");
+}
+
+// ---------------------------------------------------------------- select / commit
+static const int kPartLen = 32768;
+
+static void select_plan(int32_t V, int* nparts, int* part_len) {
+    int pl = kPartLen;
+    if (V < pl) pl = (V + 3) / 4 * 4;
+    *part_len = pl;
+    *nparts = (V + pl - 1) / pl;
+}
+
+extern "C" size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V) {
+    if (B < 1 || W < 1 || W > 64 || V < 1) return 0;
+    int np, pl;
+    select_plan(V, &np, &pl);
+    const size_t part = ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256;
+    return part + ((size_t)B * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
+extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float* logits, int32_t* tok,
+                                   uint8_t* filled, int32_t* pos, int32_t* ctx_len, int32_t* n_commit,
+                                   int32_t* committed, int32_t* argmax_out, float* entropy_out, float alpha,
+                                   float tau, int32_t mask_id, void* workspace, size_t ws_bytes, void* stream) {
+    if (B < 1 || W < 1 || W > 64 || V < 1)
+        return fail(WEDLM_ERR_SHAPE, "need B >= 1, 1 <= W <= 64, V >= 1 (B=%d W=%d V=%d)", B, W, V);
+    if ((int64_t)B * W * ((V + kPartLen - 1) / kPartLen) > (1ll << 30)) return fail(WEDLM_ERR_SHAPE, "grid too large");
+    if (!logits || !tok || !filled || !pos || !ctx_len || !n_commit || !committed)
+        return fail(WEDLM_ERR_ARG, "wedlm_select_commit: NULL device pointer");
+    if (!isfinite(alpha) || !isfinite(tau)) return fail(WEDLM_ERR_ARG, "alpha and tau must be finite");
+    const size_t need = wedlm_select_commit_workspace(B, W, V);
+    if (!workspace || ws_bytes < need)
+        return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : 0);
+    int np, pl;
+    select_plan(V, &np, &pl);
+    SelectArgs a;
+    a.logits = logits; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
+    a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;
+    a.part = static_cast<float4*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                             ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256);
+    a.B = B; a.W = W; a.V = V; a.nparts = np; a.part_len = pl;
+    a.alpha = alpha; a.tau = tau; a.mask_id = mask_id;
+    return hip_status(launch_select(a, (hipStream_t)stream), "wedlm_select_commit launch");
+}
+
+extern "C" const char* wedlm_last_error(void) { return g_err; }
+
+extern "C" const char* wedlm_version(void) { return "wedlm-mi355x 0.1 (gfx950)"; }

@@ -1,0 +1,412 @@
+// attn.hip -- windowed causal grouped-query attention of one WeDLM decode
+// step over a paged prefix KV cache (gfx950, MFMA).
+//
+// Pages: "WeDLM: Reconciling Diffusion Language Models with Standard Causal
+// Attention for Fast Inference", paper-summary page, "Key claims" (paper
+// sec. 3.2: every masked slot must see all observed tokens; sec. 4.1: after
+// the reordering a plain causal mask does this; sec. 5.2: a decode step is a
+// causal pass of the window over the cached prefix) and risewithvishwas
+// WeDLM page, "Attention Mechanism" (lower-triangular mask).
+//
+// Work decomposition.  For one (sequence b, KV head g) the M = W * (Hq/Hkv)
+// query rows (physical window row r, group head) share every K/V byte, so
+// they are packed into row tiles of RT = 32 * NW rows; wave w of a
+// work-group owns rows [32w, 32w + 32) of its tile.  The key range
+// [0, ctx_len + W) is cut into splits of split_keys keys, one work-group per
+// (b, g, row tile, split); partial (O, m, l) of several splits are merged by
+// attn_combine with the usual log-sum-exp rule.
+//
+// Per work-group the keys stream through LDS in chunks of CHUNK keys with
+// a register-staged double buffer: 16-byte coalesced global loads of whole
+// 4 KB (page, head) blocks, paged through a block-table slice held in LDS.
+//
+// Tiles are transposed so that one lane owns one query row:
+//   S^T[key][row] = K[key][:] . Q[row][:]       (A = K from LDS, B = Q in VGPRs)
+//   O^T[d][row]  += V^T[d][key] P^T[key][row]   (A = V^T via ds_read_tr16_b64,
+//                                                B = P straight from S^T's VGPRs)
+// With v_mfma_f32_32x32x16_bf16 a lane's 16 outputs are 16 keys (or 16 d)
+// of one row (lane % 32), so the online-softmax max/sum are in-lane plus
+// one exchange with lane ^ 32, and the O rescale is in-lane.  The key order
+// inside the PV contraction is permuted to match S^T's register layout; the
+// same permutation is applied to V, so the sum is unchanged.
+//
+// fp32 tensors use v_mfma_f32_32x32x2f32 with the same transposed scheme.
+#include <type_traits>
+
+#include "kernels.hpp"
+
+namespace wedlm {
+
+
+template <typename T, int D, int NW, int CHUNK>
+struct AttnCfg {
+    static constexpr int NT = 64 * NW;
+    static constexpr int RT = 32 * NW;
+    static constexpr int TB = sizeof(T);
+    static constexpr bool BF = TB == 2;
+    static constexpr int KPAD = BF ? 8 : 4;    // elements; K rows 16 B apart in bank space
+    static constexpr int VPAD = BF ? 32 : 4;   // V rows shifted by 16 banks for the transpose reads
+    static constexpr int KS = D + KPAD;
+    static constexpr int VS = D + VPAD;
+    static constexpr int ROWP = D * TB / 16;   // 16-byte pieces per key row
+    static constexpr int PIECES = CHUNK * ROWP;
+    static constexpr int PPT = PIECES / NT;    // pieces per thread per K (or V) chunk
+    static constexpr int NTILE = CHUNK / 32;
+    static constexpr int NDT = D / 32;
+    static constexpr int EPP = 16 / TB;        // elements per piece
+    static_assert(PIECES % NT == 0, "chunk must split evenly over the threads");
+};
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+template <typename T, int D, int NW, int CHUNK>
+__global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
+    using C = AttnCfg<T, D, NW, CHUNK>;
+    __shared__ __attribute__((aligned(16))) T s_k[2][CHUNK * C::KS];
+    __shared__ __attribute__((aligned(16))) T s_v[2][CHUNK * C::VS];
+    __shared__ int s_pages[kMaxSplitPages];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int hl = lane >> 5;   // lane half
+    const int col = lane & 31;  // row within the wave's 32 (S^T / O^T column)
+
+    const int pid = blockIdx.x / a.nsplit;
+    const int split = blockIdx.x - pid * a.nsplit;
+    const int rt = pid % a.row_tiles;
+    const int bk = pid / a.row_tiles;
+    const int kvh = bk % a.Hkv;
+    const int b = bk / a.Hkv;
+
+    int L = a.ctx_len[b];
+    const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
+    if (!ctx_ok) {
+        if (tid == 0 && split == 0 && rt == 0 && kvh == 0) set_status(a.status, WEDLM_DEV_BAD_CTX);
+        L = 0;
+    }
+    const int T_len = ctx_ok ? L + a.W : 0;
+    const int k_begin = split * a.split_keys;
+    const int k_end = min(T_len, k_begin + a.split_keys);
+    if (k_begin >= k_end && a.nsplit > 1) return;  // merged away by attn_combine
+
+    // block-table slice of this split
+    const int p0 = k_begin / kPage;
+    const int np = k_end > k_begin ? (k_end + kPage - 1) / kPage - p0 : 0;
+    for (int i = tid; i < np; i += C::NT) {
+        int pg = a.block_table[(size_t)b * a.max_pages + p0 + i];
+        if (pg < 0 || pg >= a.num_pages) {
+            set_status(a.status, WEDLM_DEV_BAD_PAGE);
+            pg = -1;
+        }
+        s_pages[i] = pg;
+    }
+
+    // this lane's query row
+    const int m = rt * C::RT + w * 32 + col;
+    const bool row_ok = m < a.M;
+    const int r = row_ok ? m / a.G : a.W;  // padding rows see every key (their q is 0)
+    const int h = kvh * a.G + (row_ok ? m % a.G : 0);
+    const int lim = L + r;                  // last visible key
+    const size_t q_off = (((size_t)b * a.W + (row_ok ? r : 0)) * a.Hq + h) * D;
+
+    // Q fragments (B operand of S^T = K Q^T), kept in VGPRs
+    constexpr int NQ = C::BF ? D / 16 : D / 2;
+    typedef typename std::conditional<C::BF, bf16x8, float>::type QF;
+    QF qf[NQ];
+    if constexpr (C::BF) {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + q_off);
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+            uint4 v = row_ok ? qp[s * 2 + hl] : make_uint4(0, 0, 0, 0);
+            qf[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    } else {
+        const float* qp = static_cast<const float*>(a.q) + q_off + hl * (D / 2);
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) qf[s] = row_ok ? qp[s] : 0.f;
+    }
+
+    f32x16 oacc[C::NDT];
+#pragma unroll
+    for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    __syncthreads();  // s_pages ready
+
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    uint4 kr[C::PPT], vr[C::PPT];
+
+    auto load_chunk = [&](int c) {
+        const int kb = k_begin + c * CHUNK;
+#pragma unroll
+        for (int i = 0; i < C::PPT; ++i) {
+            const int piece = tid + i * C::NT;
+            const int kc = piece / C::ROWP;
+            const int pc = piece - kc * C::ROWP;
+            const int t = kb + kc;
+            int pg = -1;
+            if (t < k_end) pg = s_pages[t / kPage - p0];
+            if (pg >= 0) {
+                const size_t off = ((((size_t)pg * a.Hkv + kvh) * kPage + (t % kPage)) * D) * C::TB + pc * 16;
+                kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
+                vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
+            } else {
+                kr[i] = make_uint4(0, 0, 0, 0);
+                vr[i] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < C::PPT; ++i) {
+            const int piece = tid + i * C::NT;
+            const int kc = piece / C::ROWP;
+            const int pc = piece - kc * C::ROWP;
+            *reinterpret_cast<uint4*>(&s_k[buf][kc * C::KS + pc * C::EPP]) = kr[i];
+            *reinterpret_cast<uint4*>(&s_v[buf][kc * C::VS + pc * C::EPP]) = vr[i];
+        }
+    };
+
+    const int n_chunks = k_end > k_begin ? (k_end - k_begin + CHUNK - 1) / CHUNK : 0;
+    if (n_chunks > 0) {
+        load_chunk(0);
+        store_chunk(0);
+    }
+    __syncthreads();
+
+    for (int c = 0; c < n_chunks; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < n_chunks) load_chunk(c + 1);
+        const T* sk = s_k[buf];
+        const T* sv = s_v[buf];
+
+        // ---- S^T = K Q^T for the chunk's 32-key tiles
+        f32x16 sacc[C::NTILE];
+#pragma unroll
+        for (int tt = 0; tt < C::NTILE; ++tt) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
+            const T* krow = sk + (tt * 32 + col) * C::KS;
+            if constexpr (C::BF) {
+#pragma unroll
+                for (int s = 0; s < NQ; ++s) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + s * 16 + hl * 8);
+                    sacc[tt] = mfma_bf16(kf, qf[s], sacc[tt]);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < NQ; ++s) sacc[tt] = mfma_f32(krow[s + hl * (D / 2)], qf[s], sacc[tt]);
+            }
+        }
+
+        // ---- online softmax (log2 domain); key of element e: 4*hl + 8*(e/4) + e%4
+        const int kb = k_begin + c * CHUNK;
+        const bool need_mask = kb + CHUNK - 1 > L;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < C::NTILE; ++tt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x = sacc[tt][e] * a.scale_log2;
+                if (need_mask) {
+                    const int t = kb + tt * 32 + hl * 4 + (e >> 2) * 8 + (e & 3);
+                    if (t > lim) x = -INFINITY;
+                }
+                sacc[tt][e] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        float lsum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < C::NTILE; ++tt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = exp2f(sacc[tt][e] - m_use);
+                sacc[tt][e] = p;
+                lsum += p;
+            }
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+        }
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int tt = 0; tt < C::NTILE; ++tt) {
+            if constexpr (C::BF) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 pf;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[tt][kk * 8 + e];
+                    // transpose-read source row/col of this lane (16-lane groups)
+                    const int key0 = tt * 32 + kk * 16 + hl * 4 + ((lane & 15) >> 2);
+                    const int dsub = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) {
+                        const T* p_lo = sv + key0 * C::VS + dt * 32 + dsub;
+                        const T* p_hi = p_lo + 8 * C::VS;
+                        const s16x4 lo = lds_read_tr(p_lo);
+                        const s16x4 hi = lds_read_tr(p_hi);
+                        const bf16x8 vf = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        oacc[dt] = mfma_bf16(vf, pf, oacc[dt]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = tt * 32 + hl * 4 + (e >> 2) * 8 + (e & 3);
+                    const float* vrow = reinterpret_cast<const float*>(sv) + key * C::VS;
+#pragma unroll
+                    for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = mfma_f32(vrow[dt * 32 + col], sacc[tt][e], oacc[dt]);
+                }
+            }
+        }
+
+        if (c + 1 < n_chunks) store_chunk(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
+    const int m_loc = m - rt * C::RT;
+    if (a.nsplit == 1) {
+        int slot = a.perm[(size_t)b * a.W + r];
+        if (slot < 0 || slot >= a.W) {
+            set_status(a.status, WEDLM_DEV_BAD_PERM);
+            return;
+        }
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        T* o = static_cast<T*>(a.out) + (((size_t)b * a.W + slot) * a.Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = dt * 32 + hl * 4 + g4 * 8;
+                if constexpr (C::BF) {
+                    uint2 pk;
+                    pk.x = f32_to_bf16(oacc[dt][g4 * 4 + 0] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][g4 * 4 + 1] * inv) << 16);
+                    pk.y = f32_to_bf16(oacc[dt][g4 * 4 + 2] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][g4 * 4 + 3] * inv) << 16);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + d) = pk;
+                } else {
+                    float4 v4 = make_float4(oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv,
+                                            oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv);
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + d) = v4;
+                }
+            }
+    } else {
+        const size_t prow = ((size_t)pid * a.nsplit + split) * C::RT + m_loc;
+        float* po = a.part_o + prow * D;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d = dt * 32 + hl * 4 + g4 * 8;
+                *reinterpret_cast<float4*>(po + d) =
+                    make_float4(oacc[dt][g4 * 4 + 0], oacc[dt][g4 * 4 + 1], oacc[dt][g4 * 4 + 2], oacc[dt][g4 * 4 + 3]);
+            }
+        if (hl == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
+    }
+}
+
+// Merge the split partials of every (b, g, row) and scatter the rows to
+// logical slot order.  One thread per output element.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+    constexpr int RPB = 256 / D;
+    const int tid = threadIdx.x;
+    const int d = tid % D;
+    const long row = (long)blockIdx.x * RPB + tid / D;
+    const int pid = (int)(row / a.RT);
+    const int m_loc = (int)(row - (long)pid * a.RT);
+    const int npid = a.B * a.Hkv * a.row_tiles;
+    if (pid >= npid) return;
+    const int rt = pid % a.row_tiles;
+    const int bk = pid / a.row_tiles;
+    const int kvh = bk % a.Hkv;
+    const int b = bk / a.Hkv;
+    const int m = rt * a.RT + m_loc;
+    if (m >= a.M) return;
+    const int r = m / a.G;
+    const int h = kvh * a.G + m % a.G;
+    const int L = a.ctx_len[b];
+    const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
+    const int T_len = ctx_ok ? L + a.W : 0;
+    const int nvalid = min(a.nsplit, (T_len + a.split_keys - 1) / a.split_keys);
+    const size_t base = (size_t)pid * a.nsplit * a.RT + m_loc;
+    float mmax = -INFINITY;
+    for (int s = 0; s < nvalid; ++s) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * a.RT].x);
+    float acc = 0.f, lsum = 0.f;
+    if (mmax != -INFINITY) {
+        for (int s = 0; s < nvalid; ++s) {
+            const float2 ml = a.part_ml[base + (size_t)s * a.RT];
+            const float wgt = exp2f(ml.x - mmax);
+            lsum += wgt * ml.y;
+            acc += wgt * a.part_o[(base + (size_t)s * a.RT) * D + d];
+        }
+    }
+    const float val = lsum > 0.f ? acc / lsum : 0.f;
+    const int slot = a.perm[(size_t)b * a.W + r];
+    if (slot < 0 || slot >= a.W) {
+        if (d == 0) set_status(a.status, WEDLM_DEV_BAD_PERM);
+        return;
+    }
+    T* o = static_cast<T*>(a.out);
+    DT<T>::store(o, (((size_t)b * a.W + slot) * a.Hq + h) * D + d, val);
+}
+
+template <typename T, int D, int NW, int CHUNK>
+static hipError_t launch_split_t(const AttnArgs& a, hipStream_t st) {
+    const int npid = a.B * a.Hkv * a.row_tiles;
+    dim3 grid((unsigned)npid * a.nsplit), block(64 * NW);
+    hipLaunchKernelGGL((attn_split<T, D, NW, CHUNK>), grid, block, 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    constexpr int RPB = 256 / D;
+    const long rows = (long)npid * a.RT;
+    dim3 g2((unsigned)((rows + RPB - 1) / RPB)), b2(256);
+    hipLaunchKernelGGL((attn_combine<T, D>), g2, b2, 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_d(const AttnArgs& a, int nw, hipStream_t st) {
+    constexpr bool BF = sizeof(T) == 2;
+    switch (nw) {
+        case 1: return launch_split_t<T, D, 1, 32>(a, st);
+        case 2: return launch_split_t<T, D, 2, BF ? 64 : 32>(a, st);
+        default: return launch_split_t<T, D, 4, BF ? 64 : 32>(a, st);
+    }
+}
+
+int attn_chunk(int dtype, int nw) { return (dtype == WEDLM_BF16 && nw > 1) ? 64 : 32; }
+
+hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {
+    if (dtype == WEDLM_F32) return D == 64 ? launch_d<float, 64>(a, nw, st) : launch_d<float, 128>(a, nw, st);
+    return D == 64 ? launch_d<bf16_t, 64>(a, nw, st) : launch_d<bf16_t, 128>(a, nw, st);
+}
+
+}  // namespace wedlm

@@ -1,0 +1,67 @@
+// kernels.hpp -- argument blocks and launchers of the decode-step kernels
+// (one struct per kernel family, passed by value as the kernel argument).
+#pragma once
+
+#include "common.hpp"
+
+namespace wedlm {
+
+constexpr int kMaxSplitPages = 512;  // LDS block-table slice of a split: split_keys <= 8192
+
+struct ReorderArgs {
+    const uint8_t* filled;
+    const int32_t* pos;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* q_phys;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_table;
+    const int32_t* ctx_len;
+    int32_t* perm;
+    int32_t* status;
+    int B, W, Hq, Hkv, D, max_pages, num_pages;
+    double log2_base;
+};
+
+struct AttnArgs {
+    const void* q;  // q_phys [B][W][Hq][D]
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* ctx_len;
+    const int32_t* perm;
+    void* out;
+    float* part_o;   // [npid][nsplit][RT][D]
+    float2* part_ml; // [npid][nsplit][RT]  (m in log2 units, l)
+    int32_t* status;
+    int B, W, Hq, Hkv, G, M, max_pages, num_pages;
+    int RT, row_tiles, nsplit, split_keys;
+    int max_ctx;       // host bound on ctx_len: the split grid covers max_ctx + W keys
+    float scale_log2;  // softmax scale * log2(e)
+};
+
+struct SelectArgs {
+    const float* logits;
+    int32_t* tok;
+    uint8_t* filled;
+    int32_t* pos;
+    int32_t* ctx_len;
+    int32_t* n_commit;
+    int32_t* committed;
+    int32_t* argmax_out;
+    float* entropy_out;
+    float4* part;         // [B*W][nparts]: (m, argmax bits, S, T)
+    uint32_t* counters;   // [B]
+    int B, W, V, nparts, part_len;
+    float alpha, tau;
+    int mask_id;
+};
+
+hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
+int attn_chunk(int dtype, int nw);
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+}  // namespace wedlm

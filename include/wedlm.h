@@ -1,0 +1,226 @@
+/*
+ * wedlm.h -- C ABI of the WeDLM streaming-decode step on MI355X (gfx950).
+ *
+ * One decode step of WeDLM (causal-attention diffusion decoding) is three
+ * calls on one HIP stream:
+ *
+ *   wedlm_reorder        Topological Reordering of the window, RoPE at the
+ *                        slots' logical positions, append of the window's
+ *                        K/V to the paged prefix cache.
+ *   wedlm_step_attn      windowed causal grouped-query attention of the
+ *                        reordered window over the cached prefix.
+ *   wedlm_select_commit  per-slot confidence (entropy, argmax) over the
+ *                        vocabulary, commit of the leading filled run, the
+ *                        distance-penalised fill rule (Eq. 11) and refill of
+ *                        the window with new masks.
+ *
+ * The operations are defined on these pages (cited by title and section):
+ *  - "WeDLM: Reconciling Diffusion Language Models with Standard Causal
+ *    Attention for Fast Inference", paper-summary page (bud-325.pages.dev):
+ *    "Key claims" (paper sec. 3.2; sec. 4.1, Eq. 5-6; sec. 5.2) and "Method"
+ *    (inference paragraph, Eq. 11);
+ *  - the same title's ICML 2026 oral page, abstract;
+ *  - risewithvishwas.com WeDLM page, "Core Technical Architecture" table.
+ *
+ * Conventions shared by every call
+ *  - Pointers named "device" are HIP device memory owned by the caller; the
+ *    library keeps no pointer after a call returns.  Host pointers are only
+ *    the shape structs and scalars.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise the device.
+ *  - Return value: WEDLM_OK, or an error status after which nothing was
+ *    enqueued; wedlm_last_error() then holds a message (thread-local).
+ *    Errors from the HIP runtime at launch are WEDLM_ERR_HIP.
+ *  - Device-side checks: conditions only the data can reveal (a context
+ *    length beyond the block table, a page id outside the pool, a
+ *    permutation entry outside the window, non-increasing positions) are
+ *    OR-ed as WEDLM_DEV_* bits into *dev_status (device int32, may be NULL);
+ *    the affected sequence is skipped (no out-of-range access is made) and
+ *    its outputs are zero (BAD_POS is reported only: RoPE is still applied
+ *    at the given positions).  The caller reads dev_status whenever it likes.
+ *  - Layouts are row-major (last index fastest).  dtype WEDLM_BF16 tensors
+ *    hold bfloat16 bit patterns; WEDLM_F32 tensors hold float.
+ *  - KV cache: pages of page_size (= 16) tokens; k_cache and v_cache are
+ *    [num_pages][Hkv][page_size][D]; token t of sequence b sits in page
+ *    block_table[b * max_pages + t / page_size], row t % page_size.
+ *  - Window state per sequence b: W slots in logical (slot) order; filled
+ *    flags (1 = observed token, 0 = mask), logical positions (strictly
+ *    increasing along the slots), ctx_len[b] = committed prefix length.
+ */
+#ifndef WEDLM_H
+#define WEDLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WEDLM_OK = 0,
+    WEDLM_ERR_ARG = 1,          /* NULL pointer or bad scalar */
+    WEDLM_ERR_SHAPE = 2,        /* inconsistent or out-of-range sizes */
+    WEDLM_ERR_UNSUPPORTED = 3,  /* valid but not built: e.g. D not 64/128 */
+    WEDLM_ERR_HIP = 4,          /* HIP runtime error at launch */
+    WEDLM_ERR_WORKSPACE = 5     /* workspace missing or too small */
+} wedlm_status;
+
+typedef enum { WEDLM_F32 = 0, WEDLM_BF16 = 1 } wedlm_dtype;
+
+/* device-side status bits */
+#define WEDLM_DEV_BAD_CTX 1u   /* ctx_len[b] < 0, ctx_len[b] + W > max_pages * page_size, or
+                                  (attention) ctx_len[b] > the call's max_ctx_len */
+#define WEDLM_DEV_BAD_PAGE 2u  /* a needed block_table entry is outside [0, num_pages) */
+#define WEDLM_DEV_BAD_PERM 4u  /* a permutation entry is outside [0, W) */
+#define WEDLM_DEV_BAD_POS 8u   /* positions negative or not strictly increasing */
+
+typedef struct {
+    int32_t B;          /* sequences */
+    int32_t W;          /* window slots per sequence, 1..64 */
+    int32_t Hq;         /* query heads */
+    int32_t Hkv;        /* KV heads; Hq % Hkv == 0, Hq / Hkv <= 16 */
+    int32_t D;          /* head dim: 64 or 128 */
+    int32_t page_size;  /* tokens per KV page: must be 16 */
+    int32_t max_pages;  /* block_table row length */
+    int32_t num_pages;  /* pages in the k_cache / v_cache pool */
+    int32_t dtype;      /* wedlm_dtype of q, k, v, caches, q_phys, out */
+} wedlm_shape;
+
+/*
+ * wedlm_reorder -- Topological Reordering + logical RoPE + KV append.
+ * (paper-summary page, "Key claims", sec. 4.1 Eq. 5-6: observed tokens move
+ * to the physical front while RoPE keeps their logical positions; "Method",
+ * inference paragraph: each step reorders the window so filled tokens come
+ * first and runs causally on the persistent cache.)
+ *
+ * For each sequence b the physical order is: filled slots in slot order,
+ * then masked slots in slot order (perm[b][r] = logical slot at physical
+ * row r).  Physical row r = slot i = perm[b][r] at position p = pos[b][i]:
+ *   q_phys[b][r][h][:]                  = RoPE_p(q[b][i][h][:])     h < Hq
+ *   k_cache at token ctx_len[b] + r     = RoPE_p(k[b][i][g][:])     g < Hkv
+ *   v_cache at token ctx_len[b] + r     = v[b][i][g][:]
+ * RoPE pairs coordinate c with c + D/2 and turns the pair by the angle
+ * p * rope_base^(-2c/D) (computed in float64, rotation in float64, result
+ * rounded once to the storage dtype).
+ *
+ *   filled  [B][W] uint8 device        pos [B][W] int32 device
+ *   q       [B][W][Hq][D]  device, logical slot order, before RoPE
+ *   k, v    [B][W][Hkv][D] device, logical slot order, before RoPE
+ *   q_phys  [B][W][Hq][D]  device out, physical order
+ *   k_cache, v_cache       device in/out; only tokens ctx_len[b] .. +W-1
+ *                          of each sequence are written
+ *   block_table [B][max_pages] int32 device; ctx_len [B] int32 device
+ *   perm    [B][W] int32 device out
+ *   dev_status  device int32 or NULL (WEDLM_DEV_BAD_CTX/PAGE/POS)
+ */
+int wedlm_reorder(const wedlm_shape *s, const uint8_t *filled, const int32_t *pos,
+                  const void *q, const void *k, const void *v, void *q_phys,
+                  void *k_cache, void *v_cache, const int32_t *block_table,
+                  const int32_t *ctx_len, int32_t *perm, double rope_base,
+                  int32_t *dev_status, void *stream);
+
+/*
+ * wedlm_step_attn_workspace -- bytes of device workspace wedlm_step_attn
+ * needs for this shape when every ctx_len[b] <= max_ctx_len.  May be 0.
+ */
+size_t wedlm_step_attn_workspace(const wedlm_shape *s, int32_t max_ctx_len);
+
+/*
+ * wedlm_step_attn -- windowed causal GQA attention of one decode step.
+ * (paper-summary page, "Key claims", sec. 3.2 and 5.2: the step is an
+ * ordinary causal pass of the window over the cached prefix; after the
+ * reordering every masked slot sees all observed tokens; risewithvishwas
+ * page, "Attention Mechanism": plain lower-triangular mask.)
+ *
+ * For sequence b (L = ctx_len[b], the window's K/V already appended at
+ * tokens L .. L+W-1 by wedlm_reorder), query head h, KV head g = h/(Hq/Hkv),
+ * physical row r:
+ *     o = sum_{t <= L + r} softmax_t(scale * q_phys[b][r][h] . K_t) V_t
+ * written to out[b][perm[b][r]][h][:] (logical slot order), in dtype.
+ *
+ *   q_phys [B][W][Hq][D] device      k_cache, v_cache  device (see top)
+ *   block_table, ctx_len, perm       device (as produced by wedlm_reorder)
+ *   out    [B][W][Hq][D] device out
+ *   scale  softmax scale; 0 means 1/sqrt(D)
+ *   max_ctx_len  host upper bound on every ctx_len[b]; sizes the split grid
+ *                (a larger ctx_len on the device is reported as BAD_CTX)
+ *   workspace / ws_bytes  device scratch of at least
+ *                wedlm_step_attn_workspace(s, max_ctx_len) bytes (NULL if 0);
+ *                contents need no initialisation and are not preserved
+ *   dev_status   device int32 or NULL (WEDLM_DEV_BAD_CTX/PAGE/PERM)
+ */
+int wedlm_step_attn(const wedlm_shape *s, const void *q_phys, const void *k_cache,
+                    const void *v_cache, const int32_t *block_table, const int32_t *ctx_len,
+                    const int32_t *perm, void *out, float scale, int32_t max_ctx_len,
+                    void *workspace, size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * wedlm_select_commit_workspace -- bytes of device workspace for
+ * wedlm_select_commit at (B, W, V).  The workspace must be zero-filled
+ * before its first use; every completed call leaves it zero-filled again,
+ * so one workspace serves any number of calls in stream order.  Two calls
+ * running at the same time must not share one workspace.
+ */
+size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V);
+
+/*
+ * wedlm_select_commit -- confidence, commit, Eq. 11 select and refill.
+ * (paper-summary page, "Method", inference paragraph, Eq. 11 and "Key
+ * claims", sec. 5.2; ICML abstract: confident tokens are committed into a
+ * growing left-to-right prefix and the window keeps a fixed size.)
+ *
+ * Per sequence b, in this order:
+ *  1. commit: k = length of the leading run of filled slots;
+ *     committed[b][i] = tok[b][i] for i < k, else -1; n_commit[b] = k;
+ *     ctx_len[b] += k.  (Those slots' K/V already sit at cache tokens
+ *     L .. L+k-1, so nothing is copied.)
+ *  2. select: for every masked slot j: a_j = argmax of logits[b][j][:]
+ *     (lowest index on ties), H_j = entropy in nats of softmax(logits[b][j]).
+ *     j0 = leftmost masked slot; Ht_j = fmaf(alpha, (float)(j - j0), H_j),
+ *     all in fp32.  Every masked slot with Ht_j < tau is filled
+ *     (tok = a_j, filled = 1); if none is, only the masked slot with the
+ *     smallest Ht_j (lowest j on ties) is.  The strict threshold, the
+ *     fallback and the tie-breaks are this library's reading of the rule.
+ *  3. refill: slots shift left by k; k masks (tok = mask_id, filled = 0)
+ *     enter at the right; pos[b][i] = ctx_len[b] + i.
+ *
+ *   logits   [B][W][V] fp32 device (rows of filled slots are not read)
+ *   tok, filled, pos [B][W], ctx_len [B]   device, updated in place
+ *   n_commit [B], committed [B][W]         device out
+ *   argmax_out [B][W] int32, entropy_out [B][W] fp32   device out or NULL;
+ *            masked slots get a_j / H_j, filled slots -1 / -1.0f
+ *   workspace / ws_bytes  see wedlm_select_commit_workspace
+ * Logits must be finite.  W <= 64, V >= 1.
+ */
+int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float *logits, int32_t *tok,
+                        uint8_t *filled, int32_t *pos, int32_t *ctx_len, int32_t *n_commit,
+                        int32_t *committed, int32_t *argmax_out, float *entropy_out,
+                        float alpha, float tau, int32_t mask_id, void *workspace,
+                        size_t ws_bytes, void *stream);
+
+/*
+ * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for
+ * this shape and bound: work-groups per (sequence, KV head, row tile)
+ * (*nsplit) and keys per work-group (*split_keys).  Either may be NULL.
+ */
+int wedlm_attn_plan(const wedlm_shape *s, int32_t max_ctx_len, int32_t *nsplit,
+                    int32_t *split_keys);
+
+/*
+ * wedlm_set_attn_split_keys -- process-wide override of the keys per
+ * split-KV work-group (a multiple of 64, 64..8192), 0 restores the
+ * automatic choice.  Affects later workspace queries and calls alike.
+ */
+int wedlm_set_attn_split_keys(int32_t keys);
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char *wedlm_last_error(void);
+
+/* Library version string. */
+const char *wedlm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WEDLM_H */

@@ -308,3 +308,50 @@ def make_logits_torch(cfg: SelectConfig, step: int, device, out=None):
         cur = rows.gather(1, flat_idx)
         rows.scatter_(1, flat_idx, torch.where(spike.view(-1, 1), torch.full_like(cur, 12.0), cur))
     return out
+
+
+# ----------------------------------------------------------------------------
+# device upload (torch tensors; storage bytes unchanged)
+# ----------------------------------------------------------------------------
+def as_torch(x: np.ndarray, dtype: str, device):
+    """numpy storage array -> torch tensor on `device` (bf16 bits viewed as bfloat16)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+def torch_storage_to_f64(t, dtype: str) -> np.ndarray:
+    """torch tensor (any device) -> float64 numpy values of its storage."""
+    import torch
+    if dtype == "bf16":
+        return bf16_bits_to_f32(t.detach().cpu().view(torch.int16).numpy().view(np.uint16)).astype(np.float64)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def device_attn_inputs(inp: AttnInputs, device, with_window: bool = True):
+    """Upload one batch: window tensors, paged cache holding the prefix,
+    block table and empty outputs (q_phys, perm, out, status)."""
+    import torch
+    cfg = inp.cfg
+    dt = cfg.dtype
+    kc, vc = paged_cache(inp, inp.prefix_k, inp.prefix_v)
+    t = dict(
+        filled=torch.from_numpy(inp.filled).to(device),
+        pos=torch.from_numpy(inp.pos).to(device),
+        ctx_len=torch.from_numpy(inp.ctx_len).to(device),
+        block_table=torch.from_numpy(inp.block_table).to(device),
+        k_cache=as_torch(kc, dt, device),
+        v_cache=as_torch(vc, dt, device),
+    )
+    if with_window:
+        t["q"] = as_torch(inp.q, dt, device)
+        t["k"] = as_torch(inp.k, dt, device)
+        t["v"] = as_torch(inp.v, dt, device)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    t["q_phys"] = torch.empty((cfg.B, cfg.W, cfg.Hq, cfg.D), dtype=tdt, device=device)
+    t["out"] = torch.empty((cfg.B, cfg.W, cfg.Hq, cfg.D), dtype=tdt, device=device)
+    t["perm"] = torch.empty((cfg.B, cfg.W), dtype=torch.int32, device=device)
+    t["status"] = torch.zeros(1, dtype=torch.int32, device=device)
+    return t
