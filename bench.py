@@ -14,9 +14,13 @@ tokens in 16-token pages (shuffled), window 32 (16 observed), bf16; logits
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
-Prints one JSON line (rank 0).  The attention call is timed with HIP events
-on the stream it runs on; its algorithmic bytes (K/V of every visible key,
-read once, plus Q in and O out) per launch are divided by that time.
+Prints one JSON line (rank 0).  Three timed regions: (1) K whole streaming
+steps, bracketed by device synchronisation, give ms_per_step and the
+headline window tokens/s; (2) K back-to-back launches of the attention call
+on the final state, bracketed by HIP events on its stream, give the mean
+launch time the roofline divides the launch's algorithmic bytes (K/V of
+every visible key read once, Q in, O out) by; (3) the select/commit call
+alone, for its own bandwidth.
 """
 import argparse
 import json
@@ -45,11 +49,33 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times): the reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """Plain device-to-device copy of known size, for counter calibration."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 5
+    print(json.dumps({"copy_MiB": mib, "bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                      "GB_per_s_read_plus_write": round(2 * n * 4 / dt / 1e9, 1)}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(see the sharding paragraph of DESIGN.md)", file=sys.stderr)
@@ -83,29 +109,31 @@ def main():
     n_commit_hist = torch.zeros((total_steps, B), dtype=torch.int32, device=dev)
     committed = torch.empty((B, W), dtype=torch.int32, device=dev)
     argmax_hist = torch.empty((total_steps, B, W), dtype=torch.int32, device=dev)  # -1 on unmasked slots
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(total_steps)]
-    ev_sel = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(total_steps)]
     nsplit, split_keys = wd.wedlm_attn_plan(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
 
-    def step(i):
+    def reorder():
         wd.wedlm_reorder(filled, pos, t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"], t["v_cache"],
                          t["block_table"], ctx, t["perm"], cfg.rope_base, dev_status=t["status"])
-        ev[i][0].record()
+
+    def attention():
         wd.wedlm_step_attn(t["q_phys"], t["k_cache"], t["v_cache"], t["block_table"], ctx, t["perm"],
                            t["out"], max_ctx_len=max_ctx, workspace=ws_attn, dev_status=t["status"])
-        ev[i][1].record()
-        ev_sel[i][0].record()
+
+    def select(i):
         wd.wedlm_select_commit(logits[i % len(logits)], tok, filled, pos, ctx, n_commit_hist[i], committed,
                                scfg.alpha, scfg.tau, mask_id, ws_sel, argmax_out=argmax_hist[i])
-        ev_sel[i][1].record()
+
+    def step(i):
+        reorder()
+        attention()
+        select(i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     ctx_start = ctx.cpu().numpy().astype(np.int64)
 
+    # ---- timed region 1: K whole streaming steps, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, total_steps):
@@ -113,30 +141,58 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # ---- timed region 2: the attention call alone, K launches back to back on
+    # the stream it runs on (the state the stream ended in), bracketed by HIP
+    # events on that stream: its mean launch duration for the roofline.
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    attention()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        attention()
+    ev1.record(stream)
+    ev1.synchronize()
+    attn_avg_ms = ev0.elapsed_time(ev1) / args.steps
+    L_now = ctx.cpu().numpy().astype(np.int64)
+
+    # ---- timed region 3: the select/commit call alone on the last logits
+    # buffer (state restored after), for its own bandwidth figure
+    saved = [x.clone() for x in (tok, filled, pos, ctx)]
+    nmask = int((filled == 0).sum().item())
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for i in range(args.steps):
+        for x, y in zip((tok, filled, pos, ctx), saved):
+            x.copy_(y)
+        select(0)
+    ev3.record(stream)
+    ev3.synchronize()
+    evc0, evc1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evc0.record(stream)
+    for i in range(args.steps):
+        for x, y in zip((tok, filled, pos, ctx), saved):
+            x.copy_(y)
+    evc1.record(stream)
+    evc1.synchronize()
+    sel_ms = (ev2.elapsed_time(ev3) - evc0.elapsed_time(evc1)) / args.steps
+
     status = int(t["status"].item())
     if status != 0:
         print(f"device status {status} (bad ctx/page/perm)", file=sys.stderr)
         sys.exit(3)
     K = args.steps
     ms_step = elapsed * 1e3 / K
-    attn_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)])
-    sel_ms = np.array([ev_sel[i][0].elapsed_time(ev_sel[i][1]) for i in range(args.warmup, total_steps)])
     nc = n_commit_hist.cpu().numpy().astype(np.int64)[args.warmup:]
-    # per-launch algorithmic bytes of the attention call
     Hkv, Hq, D = cfg.Hkv, cfg.Hq, cfg.D
     eb = 2 if cfg.dtype == "bf16" else 4
-    L_steps = ctx_start[None, :] + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(nc, 0)[:-1]], 0)
-    kv_bytes = ((L_steps + W) * Hkv * D * 2 * eb).sum(1)                # K and V of every visible key
-    qo_bytes = 2 * B * W * Hq * D * eb                                   # Q in, O out
-    attn_bytes = kv_bytes + qo_bytes
-    attn_gbs = float((attn_bytes / (attn_ms * 1e-3)).mean() / 1e9)
-    mean_attn_bytes = float(attn_bytes.mean())
-    attn_avg_ms = float(attn_ms.mean())
+    # algorithmic bytes of one attention launch at the final lengths: K and V
+    # of every visible key read once, Q read, O written
+    mean_attn_bytes = float(((L_now + W) * Hkv * D * 2 * eb).sum() + 2 * B * W * Hq * D * eb)
     achieved = mean_attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     tokens_per_s = B * W / (ms_step * 1e-3)
     masked_rows = (argmax_hist[args.warmup:] >= 0).sum(dim=(1, 2)).cpu().numpy()
-    sel_bytes = masked_rows * args.vocab * 4                              # logits rows actually read
-    sel_gbs = float((sel_bytes / (sel_ms * 1e-3)).mean() / 1e9)
+    sel_bytes = nmask * args.vocab * 4                                     # logits rows actually read
+    sel_gbs = sel_bytes / (sel_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -158,10 +214,9 @@ def main():
                    "vocab": args.vocab, "split_kv": [nsplit, split_keys]},
         "steps_per_s": round(1e3 / ms_step, 2),
         "attn": {"avg_ms": round(attn_avg_ms, 5), "alg_bytes_per_launch": int(mean_attn_bytes),
-                 "GB_per_s": round(achieved, 1)},
-        "select_commit": {"avg_ms": round(float(sel_ms.mean()), 5), "masked_rows_per_step": float(masked_rows.mean()),
-                          "GB_per_s": round(sel_gbs, 1)},
-        "reorder_plus_gaps_ms": round(ms_step - attn_avg_ms - float(sel_ms.mean()), 5),
+                 "GB_per_s": round(achieved, 1), "prefix_tokens": [int(x) for x in L_now]},
+        "select_commit": {"avg_ms": round(sel_ms, 5), "masked_rows": nmask, "GB_per_s": round(sel_gbs, 1),
+                          "masked_rows_per_step_in_stream": float(masked_rows.mean())},
         "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

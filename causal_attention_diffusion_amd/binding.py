@@ -201,9 +201,9 @@ def wedlm_select_commit_workspace(B: int, W: int, V: int) -> int:
 
 
 def select_workspace_tensor(B: int, W: int, V: int, device):
-    """Zero-filled workspace for wedlm_select_commit (the calls keep it zeroed)."""
+    """Workspace for wedlm_select_commit (no initialisation needed)."""
     import torch
-    return torch.zeros(max(wedlm_select_commit_workspace(B, W, V), 1), dtype=torch.uint8, device=device)
+    return torch.empty(max(wedlm_select_commit_workspace(B, W, V), 1), dtype=torch.uint8, device=device)
 
 
 def wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit, committed, alpha: float,

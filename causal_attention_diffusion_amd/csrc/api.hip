@@ -77,6 +77,7 @@ extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const 
 
 // ---------------------------------------------------------------- attention plan
 static int32_t g_split_override = 0;
+static const int64_t kMaxContext = 64ll * kMaxSplitPages * kPage;  // 524288 keys incl. the window
 
 struct Plan {
     int nw, chunk, RT, row_tiles, nsplit, split_keys;
@@ -108,6 +109,9 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     }
     sk = (sk + p.chunk - 1) / p.chunk * p.chunk;
     if (sk > (int64_t)kMaxSplitPages * kPage) sk = (int64_t)kMaxSplitPages * kPage;
+    // the combine merges at most 64 splits per row
+    if ((T + sk - 1) / sk > 64) sk = (T + 63) / 64;
+    sk = (sk + p.chunk - 1) / p.chunk * p.chunk;
     if (sk >= T) sk = (T + p.chunk - 1) / p.chunk * p.chunk;  // one split covers everything
     p.split_keys = (int)sk;
     p.nsplit = (int)((T + sk - 1) / sk);
@@ -128,6 +132,7 @@ extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_
     int rc = check_shape(s);
     if (rc) return rc;
     if (max_ctx_len < 0) return fail(WEDLM_ERR_ARG, "max_ctx_len must be >= 0");
+    if ((int64_t)max_ctx_len + s->W > kMaxContext) return fail(WEDLM_ERR_UNSUPPORTED, "context beyond %d tokens", kMaxContext);
     Plan p = make_plan(s, max_ctx_len);
     if (nsplit) *nsplit = p.nsplit;
     if (split_keys) *split_keys = p.split_keys;
@@ -158,6 +163,9 @@ extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const v
         return fail(WEDLM_ERR_ARG, "wedlm_step_attn: NULL device pointer");
     if (max_ctx_len < 0 || (int64_t)max_ctx_len + s->W > (int64_t)s->max_pages * kPage)
         return fail(WEDLM_ERR_SHAPE, "max_ctx_len %d + W exceeds max_pages * page_size", max_ctx_len);
+    if ((int64_t)max_ctx_len + s->W > kMaxContext)
+        return fail(WEDLM_ERR_UNSUPPORTED, "context of %d tokens: built for up to %d (64 splits of 8192 keys)",
+                    max_ctx_len + s->W, kMaxContext);
     if (!(scale >= 0.f) || !isfinite(scale)) return fail(WEDLM_ERR_ARG, "scale must be finite and >= 0");
     Plan p = make_plan(s, max_ctx_len);
     if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes))
@@ -178,7 +186,7 @@ extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const v
 }
 
 // ---------------------------------------------------------------- select / commit
-static const int kPartLen = 32768;
+static const int kPartLen = 8192;  // logits per work-group: 256 threads x 8 float4
 
 static void select_plan(int32_t V, int* nparts, int* part_len) {
     int pl = kPartLen;
@@ -191,8 +199,7 @@ extern "C" size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V)
     if (B < 1 || W < 1 || W > 64 || V < 1) return 0;
     int np, pl;
     select_plan(V, &np, &pl);
-    const size_t part = ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256;
-    return part + ((size_t)B * sizeof(uint32_t) + 255) / 256 * 256;
+    return ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256;
 }
 
 extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float* logits, int32_t* tok,
@@ -214,8 +221,6 @@ extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float*
     a.logits = logits; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
     a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;
     a.part = static_cast<float4*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                             ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256);
     a.B = B; a.W = W; a.V = V; a.nparts = np; a.part_len = pl;
     a.alpha = alpha; a.tau = tau; a.mask_id = mask_id;
     return hip_status(launch_select(a, (hipStream_t)stream), "wedlm_select_commit launch");

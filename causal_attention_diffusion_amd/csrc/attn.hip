@@ -30,7 +30,9 @@
 // inside the PV contraction is permuted to match S^T's register layout; the
 // same permutation is applied to V, so the sum is unchanged.
 //
-// fp32 tensors use v_mfma_f32_32x32x2f32 with the same transposed scheme.
+// This file holds the fp32 kernel (v_mfma_f32_32x32x2f32, register-staged
+// double buffer) and the split combine shared by both dtypes; bf16 uses the
+// direct-to-LDS kernel of attn_bf16.hip with the same tile transposition.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -333,80 +335,120 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
 }
 
 // Merge the split partials of every (b, g, row) and scatter the rows to
-// logical slot order.  One thread per output element.
+// logical slot order.  A work-group takes 256 / (D/4) rows; a thread owns 4
+// consecutive d of one row (16-byte loads of the fp32 partials).  The split
+// weights 2^(m_s - M) and the merged denominator are computed once per row
+// into LDS; the split loop is unrolled by 4 so the partial loads overlap.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-    constexpr int RPB = 256 / D;
+    constexpr int D4 = D / 4;
+    constexpr int RPB = 256 / D4;
+    constexpr int MAXS = 64;                   // splits handled in LDS at once
+    __shared__ float s_w[RPB][MAXS];
+    __shared__ float s_inv[RPB];
     const int tid = threadIdx.x;
-    const int d = tid % D;
-    const long row = (long)blockIdx.x * RPB + tid / D;
+    const int lr = tid / D4;
+    const int d = (tid % D4) * 4;
+    const long row = (long)blockIdx.x * RPB + lr;
+    const int npid = a.B * a.Hkv * a.row_tiles;
     const int pid = (int)(row / a.RT);
     const int m_loc = (int)(row - (long)pid * a.RT);
-    const int npid = a.B * a.Hkv * a.row_tiles;
-    if (pid >= npid) return;
-    const int rt = pid % a.row_tiles;
-    const int bk = pid / a.row_tiles;
-    const int kvh = bk % a.Hkv;
-    const int b = bk / a.Hkv;
-    const int m = rt * a.RT + m_loc;
-    if (m >= a.M) return;
+    const bool live = pid < npid;
+    int b = 0, kvh = 0, m = 0, nvalid = 0;
+    if (live) {
+        const int rt = pid % a.row_tiles;
+        const int bk = pid / a.row_tiles;
+        kvh = bk % a.Hkv;
+        b = bk / a.Hkv;
+        m = rt * a.RT + m_loc;
+        const int L = a.ctx_len[b];
+        const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
+        const int T_len = ctx_ok ? L + a.W : 0;
+        nvalid = min(a.nsplit, (T_len + a.split_keys - 1) / a.split_keys);
+    }
+    const size_t base = live ? (size_t)pid * a.nsplit * a.RT + m_loc : 0;
+    // one thread per row computes the weights
+    if (tid % D4 == 0) {
+        float M = -INFINITY;
+        for (int s = 0; s < nvalid; ++s) M = fmaxf(M, a.part_ml[base + (size_t)s * a.RT].x);
+        float den = 0.f;
+        for (int s = 0; s < nvalid && s < MAXS; ++s) {
+            const float2 ml = a.part_ml[base + (size_t)s * a.RT];
+            const float w = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+            s_w[lr][s] = w;
+            den += w * ml.y;
+        }
+        s_inv[lr] = den > 0.f ? 1.f / den : 0.f;
+    }
+    __syncthreads();
+    if (!live || m >= a.M) return;
+    const int ns = nvalid < MAXS ? nvalid : MAXS;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* po = a.part_o + base * D + d;
+    const size_t stride = (size_t)a.RT * D;
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+        const float4 v0 = *reinterpret_cast<const float4*>(po + (s + 0) * stride);
+        const float4 v1 = *reinterpret_cast<const float4*>(po + (s + 1) * stride);
+        const float4 v2 = *reinterpret_cast<const float4*>(po + (s + 2) * stride);
+        const float4 v3 = *reinterpret_cast<const float4*>(po + (s + 3) * stride);
+        const float w0 = s_w[lr][s], w1 = s_w[lr][s + 1], w2 = s_w[lr][s + 2], w3 = s_w[lr][s + 3];
+        acc.x += w0 * v0.x + w1 * v1.x + w2 * v2.x + w3 * v3.x;
+        acc.y += w0 * v0.y + w1 * v1.y + w2 * v2.y + w3 * v3.y;
+        acc.z += w0 * v0.z + w1 * v1.z + w2 * v2.z + w3 * v3.z;
+        acc.w += w0 * v0.w + w1 * v1.w + w2 * v2.w + w3 * v3.w;
+    }
+    for (; s < ns; ++s) {
+        const float4 v0 = *reinterpret_cast<const float4*>(po + s * stride);
+        const float w0 = s_w[lr][s];
+        acc.x += w0 * v0.x; acc.y += w0 * v0.y; acc.z += w0 * v0.z; acc.w += w0 * v0.w;
+    }
+    const float inv = s_inv[lr];
     const int r = m / a.G;
     const int h = kvh * a.G + m % a.G;
-    const int L = a.ctx_len[b];
-    const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
-    const int T_len = ctx_ok ? L + a.W : 0;
-    const int nvalid = min(a.nsplit, (T_len + a.split_keys - 1) / a.split_keys);
-    const size_t base = (size_t)pid * a.nsplit * a.RT + m_loc;
-    float mmax = -INFINITY;
-    for (int s = 0; s < nvalid; ++s) mmax = fmaxf(mmax, a.part_ml[base + (size_t)s * a.RT].x);
-    float acc = 0.f, lsum = 0.f;
-    if (mmax != -INFINITY) {
-        for (int s = 0; s < nvalid; ++s) {
-            const float2 ml = a.part_ml[base + (size_t)s * a.RT];
-            const float wgt = exp2f(ml.x - mmax);
-            lsum += wgt * ml.y;
-            acc += wgt * a.part_o[(base + (size_t)s * a.RT) * D + d];
-        }
-    }
-    const float val = lsum > 0.f ? acc / lsum : 0.f;
     const int slot = a.perm[(size_t)b * a.W + r];
     if (slot < 0 || slot >= a.W) {
         if (d == 0) set_status(a.status, WEDLM_DEV_BAD_PERM);
         return;
     }
-    T* o = static_cast<T*>(a.out);
-    DT<T>::store(o, (((size_t)b * a.W + slot) * a.Hq + h) * D + d, val);
+    T* o = static_cast<T*>(a.out) + (((size_t)b * a.W + slot) * a.Hq + h) * D + d;
+    DT<T>::store(o, 0, acc.x * inv);
+    DT<T>::store(o, 1, acc.y * inv);
+    DT<T>::store(o, 2, acc.z * inv);
+    DT<T>::store(o, 3, acc.w * inv);
 }
 
-template <typename T, int D, int NW, int CHUNK>
-static hipError_t launch_split_t(const AttnArgs& a, hipStream_t st) {
-    const int npid = a.B * a.Hkv * a.row_tiles;
-    dim3 grid((unsigned)npid * a.nsplit), block(64 * NW);
-    hipLaunchKernelGGL((attn_split<T, D, NW, CHUNK>), grid, block, 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.nsplit == 1) return e;
-    constexpr int RPB = 256 / D;
-    const long rows = (long)npid * a.RT;
+template <typename T, int D>
+static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
+    constexpr int RPB = 256 / (D / 4);
+    const long rows = (long)a.B * a.Hkv * a.row_tiles * a.RT;
     dim3 g2((unsigned)((rows + RPB - 1) / RPB)), b2(256);
     hipLaunchKernelGGL((attn_combine<T, D>), g2, b2, 0, st, a);
     return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t launch_d(const AttnArgs& a, int nw, hipStream_t st) {
-    constexpr bool BF = sizeof(T) == 2;
-    switch (nw) {
-        case 1: return launch_split_t<T, D, 1, 32>(a, st);
-        case 2: return launch_split_t<T, D, 2, BF ? 64 : 32>(a, st);
-        default: return launch_split_t<T, D, 4, BF ? 64 : 32>(a, st);
-    }
+template <int D, int NW>
+static hipError_t launch_f32_t(const AttnArgs& a, hipStream_t st) {
+    const int npid = a.B * a.Hkv * a.row_tiles;
+    hipLaunchKernelGGL((attn_split<float, D, NW, 32>), dim3((unsigned)npid * a.nsplit), dim3(64 * NW), 0, st, a);
+    return hipGetLastError();
 }
 
-int attn_chunk(int dtype, int nw) { return (dtype == WEDLM_BF16 && nw > 1) ? 64 : 32; }
+int attn_chunk(int dtype, int nw) { return dtype == WEDLM_BF16 ? 64 : 32; }
+
+hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st);
 
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {
-    if (dtype == WEDLM_F32) return D == 64 ? launch_d<float, 64>(a, nw, st) : launch_d<float, 128>(a, nw, st);
-    return D == 64 ? launch_d<bf16_t, 64>(a, nw, st) : launch_d<bf16_t, 128>(a, nw, st);
+    hipError_t e;
+    if (dtype == WEDLM_F32) {
+        if (D == 64) e = nw == 1 ? launch_f32_t<64, 1>(a, st) : nw == 2 ? launch_f32_t<64, 2>(a, st) : launch_f32_t<64, 4>(a, st);
+        else e = nw == 1 ? launch_f32_t<128, 1>(a, st) : nw == 2 ? launch_f32_t<128, 2>(a, st) : launch_f32_t<128, 4>(a, st);
+    } else {
+        e = launch_attn_bf16_split(a, D, nw, st);
+    }
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    if (dtype == WEDLM_F32) return D == 64 ? launch_combine_t<float, 64>(a, st) : launch_combine_t<float, 128>(a, st);
+    return D == 64 ? launch_combine_t<bf16_t, 64>(a, st) : launch_combine_t<bf16_t, 128>(a, st);
 }
 
 }  // namespace wedlm

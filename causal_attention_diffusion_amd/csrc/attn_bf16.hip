@@ -1,0 +1,449 @@
+// attn_bf16.hip -- bf16 windowed causal GQA attention of one WeDLM decode
+// step over a paged KV cache, streamed through LDS by direct global->LDS
+// loads (gfx950).
+//
+// Pages: "WeDLM: Reconciling Diffusion Language Models with Standard Causal
+// Attention for Fast Inference", paper-summary page, "Key claims" (paper
+// sec. 3.2, 4.1, 5.2: after the reordering a plain causal mask lets every
+// masked slot see all observed tokens; a decode step is a causal pass of
+// the window over the cached prefix) and risewithvishwas WeDLM page,
+// "Attention Mechanism" (lower-triangular mask).
+//
+// What differs from the fp32 kernel (attn.hip) is how K/V reach LDS:
+//  * global_load_lds_dwordx4 writes each wave's 16-byte loads straight into
+//    LDS (1 KB per wave instruction), so no VGPRs hold data in flight and an
+//    NST-stage ring of 64-key chunks keeps NST-1 chunks (96 KB at D = 128)
+//    in flight per work-group;
+//  * completion is tracked per wave with s_waitcnt vmcnt(n) and made visible
+//    to the other waves by one s_barrier per chunk;
+//  * LDS rows are unpadded; 16-byte chunks are XOR-swizzled per key (the
+//    lane that fills LDS slot (key, c) loads global chunk c ^ f(key)), so
+//    the K reads (ds_read_b128, 16 keys per 16 lanes) and the V transpose
+//    reads (ds_read_b64_tr_b16, 4 keys x 4 chunks per 32 lanes) spread
+//    over all banks.
+// Work split: 8 waves = NRG row groups (32 query rows each) x NKG key
+// groups.  The key group of a wave owns every NKG-th 32-key tile and keeps
+// its own online-softmax state; the key groups are merged through LDS at
+// the end, then the work-group writes either the final rows (one split)
+// or a split partial for attn_combine.
+#include "kernels.hpp"
+
+namespace wedlm {
+
+template <int D>
+struct Bf16Cfg {
+    static constexpr int NWAVES = 8;
+    static constexpr int NT = 64 * NWAVES;
+    static constexpr int SK = 64;                    // keys per stage
+    static constexpr int RC = D * 2 / 16;            // 16-byte chunks per key row (8 or 16)
+    static constexpr int NST = D == 128 ? 4 : 8;     // ring stages
+    static constexpr int KBYTES = SK * D * 2;        // K bytes per stage
+    static constexpr int STAGE = 2 * KBYTES;         // K then V
+    static constexpr int LPS = STAGE / 1024 / NWAVES; // DMA instructions per wave per stage
+    static constexpr int NDT = D / 32;
+    static_assert(LPS * 1024 * NWAVES == STAGE, "stage must split into whole wave loads");
+};
+
+constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised P
+
+__device__ __forceinline__ int swz_k(int key, int c, int rc) { return c ^ (key & (rc - 1)); }
+__device__ __forceinline__ int swz_v(int key, int c, int rc) { return c ^ ((4 * (key & 3)) & (rc - 1)); }
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void block_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait until at most `ahead` stages (LPS loads each) of this wave's DMA are
+// still in flight, i.e. the stage issued `ahead` stages before the last one
+// has landed.  `ahead` is clamped to MAXA (stricter waits stay correct).
+template <int LPS, int MAXA>
+__device__ __forceinline__ void wait_stage(int ahead) {
+    static_assert(MAXA <= 7 && 7 * LPS < 64, "vmcnt range");
+    if (ahead > MAXA) ahead = MAXA;
+    switch (ahead) {
+        case 7: wait_vm<(7 * LPS) & 63>(); break;
+        case 6: wait_vm<(6 * LPS) & 63>(); break;
+        case 5: wait_vm<(5 * LPS) & 63>(); break;
+        case 4: wait_vm<4 * LPS>(); break;
+        case 3: wait_vm<3 * LPS>(); break;
+        case 2: wait_vm<2 * LPS>(); break;
+        case 1: wait_vm<LPS>(); break;
+        default: wait_vm<0>(); break;
+    }
+}
+
+// Transpose reads of V for one 16-key MFMA k-step, all d-tiles at once:
+// rows key0 (+ OFF) and key0 + 8 (+ OFF + 8 rows) of each d-tile address.
+// Issued from inline asm with their own lgkmcnt wait: the compiler's wait
+// insertion would otherwise put an s_waitcnt vmcnt(0) in front of every
+// ds_read_b64_tr_b16 (it cannot tell them apart from the in-flight DMA
+// writes of later stages), which would drain the prefetch ring.
+template <int OFF, int ROWB>
+__device__ __forceinline__ void tr_reads4(const uint32_t (&ad)[4], s16x4 (&lo)[4], s16x4 (&hi)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+          "=&v"(hi[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF), "i"(OFF + 8 * ROWB));
+}
+template <int OFF, int ROWB>
+__device__ __forceinline__ void tr_reads2(const uint32_t (&ad)[2], s16x4 (&lo)[2], s16x4 (&hi)[2]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(hi[0]), "=&v"(hi[1])
+        : "v"(ad[0]), "v"(ad[1]), "i"(OFF), "i"(OFF + 8 * ROWB));
+}
+
+// Value of lane l ^ 32 (v_permlane32_swap: the upper half of the first
+// operand trades places with the lower half of the second).
+__device__ __forceinline__ float other_half(float x, int hl) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(hl ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);  // low 32 bits of a shared-aperture address
+}
+
+template <int D, int NRG>
+__global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
+    using C = Bf16Cfg<D>;
+    constexpr int NKG = C::NWAVES / NRG;
+    constexpr int RT = 32 * NRG;
+    constexpr int MSTRIDE = D + 4;                              // merge rows, floats
+    constexpr int RING = C::NST * C::STAGE;              // NST slots of (K, V)
+    constexpr int MERGE = NKG * RT * MSTRIDE * 4;
+    constexpr int SMEM = RING > MERGE ? RING : MERGE;
+    __shared__ __attribute__((aligned(1024))) char s_ring[SMEM];
+    __shared__ float2 s_ml[NKG][RT];
+    __shared__ int s_pages[kMaxSplitPages];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int rg = w % NRG;          // row group
+    const int kg = w / NRG;          // key group
+    const int hl = lane >> 5;
+    const int col = lane & 31;
+
+    const int pid = blockIdx.x / a.nsplit;
+    const int split = blockIdx.x - pid * a.nsplit;
+    const int rt = pid % a.row_tiles;
+    const int bk = pid / a.row_tiles;
+    const int kvh = bk % a.Hkv;
+    const int b = bk / a.Hkv;
+
+    int L = a.ctx_len[b];
+    const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
+    if (!ctx_ok) {
+        if (tid == 0 && split == 0 && rt == 0 && kvh == 0) set_status(a.status, WEDLM_DEV_BAD_CTX);
+        L = 0;
+    }
+    const int T_len = ctx_ok ? L + a.W : 0;
+    const int k_begin = split * a.split_keys;
+    const int k_end = min(T_len, k_begin + a.split_keys);
+    if (k_begin >= k_end && a.nsplit > 1) return;  // nothing here; attn_combine skips this split
+
+    const int p0 = k_begin / kPage;
+    const int np = k_end > k_begin ? (k_end + kPage - 1) / kPage - p0 : 0;
+    for (int i = tid; i < np; i += C::NT) {
+        int pg = a.block_table[(size_t)b * a.max_pages + p0 + i];
+        if (pg < 0 || pg >= a.num_pages) {
+            set_status(a.status, WEDLM_DEV_BAD_PAGE);
+            pg = 0;  // stay in bounds; the sequence's result is meaningless and flagged
+        }
+        s_pages[i] = pg;
+    }
+
+    // this lane's query row
+    const int m = rt * RT + rg * 32 + col;
+    const bool row_ok = m < a.M;
+    const int r = row_ok ? m / a.G : a.W;
+    const int h = kvh * a.G + (row_ok ? m % a.G : 0);
+    const int lim = L + r;
+    bf16x8 qf[D / 16];
+    {
+        const size_t q_off = (((size_t)b * a.W + (row_ok ? r : 0)) * a.Hq + h) * D;
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + q_off);
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const uint4 v = row_ok ? qp[s * 2 + hl] : make_uint4(0, 0, 0, 0);
+            qf[s] = __builtin_bit_cast(bf16x8, v);
+        }
+    }
+    f32x16 oacc[C::NDT];
+#pragma unroll
+    for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    __syncthreads();  // s_pages visible; Q loads may still be in flight (waited below)
+    wait_vm<0>();     // the Q loads count in vmcnt: retire them before the ring accounting starts
+
+    const int n_stages = k_end > k_begin ? (k_end - k_begin + C::SK - 1) / C::SK : 0;
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int last_key = k_end - 1;
+
+    // DMA plan.  A stage is 4 pages of K and 4 pages of V (64 keys, one
+    // (page, head) block each).  Wave w loads one whole block per stage:
+    // waves 0..3 the K pages, waves 4..7 the V pages of ring slot st % NST.
+    // The lane offsets inside a block (row,
+    // swizzled chunk) never change, so a stage costs one page-table read per
+    // wave and LPS loads with a uniform base.
+    constexpr int ROWB = D * 2;
+    constexpr int KPB = 1024 / ROWB;                 // keys per 1 KB block
+    const bool wv_v = w >= 4;
+    const int wpage = w & 3;
+    const char* wbase = wv_v ? vbase : kbase;
+    uint32_t lane_off[C::LPS];
+    int lane_kin[C::LPS];
+#pragma unroll
+    for (int n = 0; n < C::LPS; ++n) {
+        const int kin = n * KPB + lane / (ROWB / 16);
+        const int cs = lane % (ROWB / 16);
+        const int c = wv_v ? swz_v(kin, cs, C::RC) : swz_k(kin, cs, C::RC);
+        lane_kin[n] = kin;
+        lane_off[n] = (uint32_t)(kin * ROWB + c * 16);
+    }
+    static_assert(C::LPS * KPB == kPage, "one wave loads exactly one page block per stage");
+    auto kslot = [&](int st) { return s_ring + (st % C::NST) * C::STAGE; };
+    auto vslot = [&](int st) { return kslot(st) + C::KBYTES; };
+    auto issue = [&](int st) {
+        char* dst = (wv_v ? vslot(st) : kslot(st)) + wpage * C::LPS * 1024;
+        const int kp = k_begin + st * C::SK + wpage * kPage;    // first key of this wave's page
+        if (kp + kPage - 1 <= last_key) {
+            const int pg = __builtin_amdgcn_readfirstlane(s_pages[kp / kPage - p0]);  // wave-uniform
+            const char* pbase = wbase + ((size_t)pg * a.Hkv + kvh) * (kPage * ROWB);
+#pragma unroll
+            for (int n = 0; n < C::LPS; ++n)
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(pbase + lane_off[n]),
+                    (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(dst + n * 1024)), 16, 0, 0);
+        } else {
+            // the sequence ends inside (or before) this page: rows past the
+            // last key reload the last key's row (finite data, masked later)
+#pragma unroll
+            for (int n = 0; n < C::LPS; ++n) {
+                int t = kp + lane_kin[n];
+                if (t > last_key) t = last_key;
+                const int pg = s_pages[t / kPage - p0];
+                const size_t goff = (((size_t)pg * a.Hkv + kvh) * kPage + (t % kPage)) * ROWB +
+                                    (lane_off[n] % ROWB);
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)(wbase + goff),
+                    (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(dst + n * 1024)), 16, 0, 0);
+            }
+        }
+    };
+
+    // Per-lane V transpose-read addresses inside a V slot: the 16-lane groups
+    // read rows key0 = hl*4 + (lane&15)/4 (+ tile/k-step rows, immediates)
+    // at d = dt*32 + 16*((lane>>4)&1) + 4*(lane&3); the swizzle depends on
+    // key & 3 only, which the immediates do not change.
+    const int vkey = hl * 4 + ((lane & 15) >> 2);
+    int vcol[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+        vcol[dt] = vkey * ROWB + swz_v(vkey, d / 8, C::RC) * 16 + (d % 8) * 2;
+    }
+    // P^T fragments of the current tile (bf16, two 16-key k-steps)
+    bf16x8 pprev[2];
+    auto pv = [&](int tt, int st) {
+        const uint32_t vb = lds_u32(vslot(st));
+        uint32_t va[C::NDT];
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) va[dt] = vb + vcol[dt];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            s16x4 lo[C::NDT], hi[C::NDT];
+            if constexpr (C::NDT == 4) {
+                if (tt == 0 && kk == 0) tr_reads4<0, ROWB>(va, lo, hi);
+                else if (tt == 0) tr_reads4<16 * ROWB, ROWB>(va, lo, hi);
+                else if (kk == 0) tr_reads4<32 * ROWB, ROWB>(va, lo, hi);
+                else tr_reads4<48 * ROWB, ROWB>(va, lo, hi);
+            } else {
+                if (tt == 0 && kk == 0) tr_reads2<0, ROWB>(va, lo, hi);
+                else if (tt == 0) tr_reads2<16 * ROWB, ROWB>(va, lo, hi);
+                else if (kk == 0) tr_reads2<32 * ROWB, ROWB>(va, lo, hi);
+                else tr_reads2<48 * ROWB, ROWB>(va, lo, hi);
+            }
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pprev[kk], oacc[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    const int npro = n_stages < C::NST - 1 ? n_stages : C::NST - 1;
+    for (int st = 0; st < npro; ++st) issue(st);
+    for (int st = 0; st < n_stages; ++st) {
+        // this wave's loads of stage st landed (issued stages end at
+        // min(st+NST-2, n_stages-1)); the barrier makes every wave's part
+        // visible and frees slot (st-1) % NST for the next DMA
+        wait_stage<C::LPS, C::NST - 2>(min(C::NST - 2, n_stages - 1 - st));
+        block_sync();
+        if (st + C::NST - 1 < n_stages) issue(st + C::NST - 1);
+
+#pragma unroll
+        for (int tt = 0; tt < C::SK / 32; ++tt) {
+            if (((st * (C::SK / 32) + tt) % NKG) != kg) continue;
+            // S^T = K Q^T for this wave's 32-key tile
+            const int key = tt * 32 + col;
+            const char* krow = kslot(st) + key * ROWB;
+            bf16x8 kf[D / 16];
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + swz_k(key, 2 * s + hl, C::RC) * 16);
+            f32x16 sacc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+
+            // online softmax in the log2 domain with a lazily moved reference:
+            // m_run only moves when a row's tile maximum exceeds it by more than
+            // kLazy (then P <= 2^kLazy stays exact enough in bf16 and the fp32
+            // sums), so the O rescale is rare.
+            const int tb = k_begin + st * C::SK + tt * 32;   // first key of the tile
+            if (tb + 31 > L) {        // uniform: only tiles reaching past the cached prefix
+                asm volatile("");     // keep this a branch (no speculation into every tile)
+                const int thr = lim - tb - hl * 4;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if ((e >> 2) * 8 + (e & 3) > thr) sacc[e] = -INFINITY;
+            }
+            float mx = sacc[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+            mx = fmaxf(mx, other_half(mx, hl)) * a.scale_log2;
+            if (__any(mx > m_run + kLazy)) {
+                const float m_new = mx > m_run + kLazy ? mx : m_run;
+                const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            float lsum = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kk * 8 + e], a.scale_log2, -m_use));
+                    lsum += p;
+                    pprev[kk][e] = (__bf16)p;
+                }
+            l_run += lsum;
+            // O^T += V^T P^T
+            pv(tt, st);
+        }
+    }
+
+    // ---- merge the key groups through LDS
+    const float l_tot = l_run + other_half(l_run, hl);
+    wait_vm<0>();
+    wait_lgkm0();
+    block_sync();   // ring no longer read by anyone
+    float* mg = reinterpret_cast<float*>(s_ring);
+    {
+        const int row = rg * 32 + col;
+        float* dst = mg + ((size_t)kg * RT + row) * MSTRIDE;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                *reinterpret_cast<float4*>(dst + dt * 32 + hl * 4 + g4 * 8) =
+                    make_float4(oacc[dt][g4 * 4 + 0], oacc[dt][g4 * 4 + 1], oacc[dt][g4 * 4 + 2], oacc[dt][g4 * 4 + 3]);
+        if (hl == 0) s_ml[kg][row] = make_float2(m_run, l_tot);
+    }
+    __syncthreads();
+
+    constexpr int D4 = D / 4;
+    for (int idx = tid; idx < RT * D4; idx += C::NT) {
+        const int row = idx / D4;
+        const int d = (idx % D4) * 4;
+        const int mm = rt * RT + row;
+        if (mm >= a.M) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < NKG; ++g) M = fmaxf(M, s_ml[g][row].x);
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float Ls = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int g = 0; g < NKG; ++g) {
+                const float2 ml = s_ml[g][row];
+                const float wgt = __builtin_amdgcn_exp2f(ml.x - M);
+                Ls += wgt * ml.y;
+                const float4 v = *reinterpret_cast<const float4*>(mg + ((size_t)g * RT + row) * MSTRIDE + d);
+                o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
+            }
+        }
+        if (a.nsplit == 1) {
+            const int rr = mm / a.G;
+            const int hh = kvh * a.G + mm % a.G;
+            const int slot = a.perm[(size_t)b * a.W + rr];
+            if (slot < 0 || slot >= a.W) {
+                set_status(a.status, WEDLM_DEV_BAD_PERM);
+                continue;
+            }
+            const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+            uint16_t* op = static_cast<uint16_t*>(a.out) + (((size_t)b * a.W + slot) * a.Hq + hh) * D + d;
+            uint2 pk;
+            pk.x = f32_to_bf16(o.x * inv) | ((uint32_t)f32_to_bf16(o.y * inv) << 16);
+            pk.y = f32_to_bf16(o.z * inv) | ((uint32_t)f32_to_bf16(o.w * inv) << 16);
+            *reinterpret_cast<uint2*>(op) = pk;
+        } else {
+            const size_t prow = ((size_t)pid * a.nsplit + split) * RT + row;
+            *reinterpret_cast<float4*>(a.part_o + prow * D + d) = o;
+            if (d == 0) a.part_ml[prow] = make_float2(M, Ls);
+        }
+    }
+}
+
+template <int D, int NRG>
+static hipError_t launch_bf16_t(const AttnArgs& a, hipStream_t st) {
+    const int npid = a.B * a.Hkv * a.row_tiles;
+    hipLaunchKernelGGL((attn_split_bf16<D, NRG>), dim3((unsigned)npid * a.nsplit), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st) {
+    if (D == 64) {
+        if (nrg == 1) return launch_bf16_t<64, 1>(a, st);
+        if (nrg == 2) return launch_bf16_t<64, 2>(a, st);
+        return launch_bf16_t<64, 4>(a, st);
+    }
+    if (nrg == 1) return launch_bf16_t<128, 1>(a, st);
+    if (nrg == 2) return launch_bf16_t<128, 2>(a, st);
+    return launch_bf16_t<128, 4>(a, st);
+}
+
+}  // namespace wedlm

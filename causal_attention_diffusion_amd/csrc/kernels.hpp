@@ -53,7 +53,6 @@ struct SelectArgs {
     int32_t* argmax_out;
     float* entropy_out;
     float4* part;         // [B*W][nparts]: (m, argmax bits, S, T)
-    uint32_t* counters;   // [B]
     int B, W, V, nparts, part_len;
     float alpha, tau;
     int mask_id;

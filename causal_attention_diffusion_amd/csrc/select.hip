@@ -10,19 +10,27 @@
 // 5.2); ICML abstract (a growing left-to-right committed prefix, fixed
 // window).
 //
-// One launch.  Work-group (b, j, part) streams part `part` of the logits
-// row of slot j when that slot is masked (rows of filled slots are never
-// read): per thread an online (max, first argmax, S = sum e^{z-m},
-// T = sum (z-m) e^{z-m}) over 16-byte loads, then a wave/LDS merge, and the
-// partial is stored in the workspace.  Every work-group of sequence b then
-// bumps b's arrival counter; the last one to arrive merges the row partials
-// (H = ln S - T/S) and one wave, one lane per slot, runs commit / select /
-// refill with ballots and shuffles, and puts the counter back to zero.
+// Two launches.  vocab_stats: work-group (b, j, part) streams part `part` of
+// the logits row of slot j when that slot is masked (rows of filled slots
+// are never read): per thread an online (max, first argmax, S = sum 2^u,
+// T = sum u 2^u with u = (z - max) log2 e) over 16-byte loads issued 8 at a
+// time, then a wave/LDS merge, and the row-part partial goes to the
+// workspace.  commit_select_refill: one wave per sequence, one lane per
+// slot, merges its rows' partials (H = ln S - ln2 T/S) and runs commit /
+// select / refill with ballots and shuffles.  The kernel boundary orders
+// the two; an in-kernel last-arrival scheme would need an agent-scope
+// release fence per work-group, which writes back L2 and cost more than a
+// second launch.
 #include "kernels.hpp"
 
 namespace wedlm {
 
+constexpr int kVecPerThread = 8;  // float4 loads per thread per full part
 
+
+// Online statistics of a logits row slice: max m, first argmax a,
+// S = sum 2^{u} and T = sum u 2^{u} with u = (z - m) * log2(e), so that the
+// entropy in nats is H = ln S - ln(2) T / S.
 struct Stat {
     float m;
     int a;
@@ -36,28 +44,72 @@ __device__ __forceinline__ Stat merge(const Stat& x, const Stat& y) {
     Stat o;
     o.m = fmaxf(x.m, y.m);
     o.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
-    const float dx = x.m - o.m, dy = y.m - o.m;
-    const float ex = exp2f(dx * kLog2e), ey = exp2f(dy * kLog2e);
+    const float dx = (x.m - o.m) * kLog2e, dy = (y.m - o.m) * kLog2e;
+    const float ex = __builtin_amdgcn_exp2f(dx), ey = __builtin_amdgcn_exp2f(dy);
     o.s = x.s * ex + y.s * ey;
-    o.t = ex * (x.t + dx * x.s) + ey * (y.t + dy * y.s);
+    o.t = ex * fmaf(dx, x.s, x.t) + ey * fmaf(dy, y.s, y.t);
     return o;
 }
 
-__device__ __forceinline__ void accum(Stat& st, float z, int idx) {
-    if (z > st.m) {
-        if (st.s != 0.f) {
-            const float dm = st.m - z;
-            const float sc = exp2f(dm * kLog2e);
-            st.t = sc * (st.t + dm * st.s);
-            st.s *= sc;
-        }
-        st.m = z;
-        st.a = idx;
+// Move the reference maximum of st up to bm (new first argmax ba).
+__device__ __forceinline__ void raise_max(Stat& st, float bm, int ba) {
+    if (st.s != 0.f) {
+        const float d = (st.m - bm) * kLog2e;
+        const float sc = __builtin_amdgcn_exp2f(d);
+        st.t = sc * fmaf(d, st.s, st.t);
+        st.s *= sc;
     }
-    const float u = z - st.m;
-    const float e = exp2f(u * kLog2e);
-    st.s += e;
-    st.t += u * e;
+    st.m = bm;
+    st.a = ba;
+}
+
+// Add exp terms of one value (its maximum is already folded into st.m).
+__device__ __forceinline__ void add_term(float& s, float& t, float z, float m) {
+    // (z - m) first: exact 0 at the maximum, so a row with one dominant
+    // logit gets exactly S = 1, T = 0 there (H = 0 for a certain row)
+    const float u = (z - m) * kLog2e;
+    const float e = __builtin_amdgcn_exp2f(u);
+    s += e;
+    t = fmaf(u, e, t);
+}
+
+// Fold K float4 (element j of v[k] has index base + 1024 k + j, increasing
+// in visiting order) into st: one max test per batch.
+template <int K>
+__device__ __forceinline__ void accum_vec(Stat& st, const float4 (&v)[K], int base) {
+    float bm = fmaxf(fmaxf(v[0].x, v[0].y), fmaxf(v[0].z, v[0].w));
+#pragma unroll
+    for (int k = 1; k < K; ++k) bm = fmaxf(bm, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+    if (bm > st.m) {
+        int ba = 0x7fffffff;
+#pragma unroll
+        for (int k = K - 1; k >= 0; --k) {   // backwards, so the first match wins
+            const int i0 = base + 1024 * k;
+            if (v[k].w == bm) ba = i0 + 3;
+            if (v[k].z == bm) ba = i0 + 2;
+            if (v[k].y == bm) ba = i0 + 1;
+            if (v[k].x == bm) ba = i0;
+        }
+        raise_max(st, bm, ba);
+    }
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        add_term(s, t, v[k].x, st.m);
+        add_term(s, t, v[k].y, st.m);
+        add_term(s, t, v[k].z, st.m);
+        add_term(s, t, v[k].w, st.m);
+    }
+    st.s += s;
+    st.t += t;
+}
+
+__device__ __forceinline__ void accum_one(Stat& st, float z, int idx) {
+    if (z > st.m) raise_max(st, z, idx);
+    float s = 0.f, t = 0.f;
+    add_term(s, t, z, st.m);
+    st.s += s;
+    st.t += t;
 }
 
 __device__ __forceinline__ Stat shfl_xor_stat(const Stat& x, int mask) {
@@ -70,7 +122,7 @@ __device__ __forceinline__ Stat shfl_xor_stat(const Stat& x, int mask) {
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(256) void vocab_select_commit(SelectArgs a) {
+__global__ __launch_bounds__(256) void vocab_stats(SelectArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -79,7 +131,6 @@ __global__ __launch_bounds__(256) void vocab_select_commit(SelectArgs a) {
     const int b = row / a.W;
 
     __shared__ Stat s_red[4];
-    __shared__ int s_last;
 
     const bool masked = a.filled[row] == 0;
     if (masked) {
@@ -88,26 +139,24 @@ __global__ __launch_bounds__(256) void vocab_select_commit(SelectArgs a) {
         const float* z = a.logits + (size_t)row * a.V;
         Stat st{-INFINITY, 0x7fffffff, 0.f, 0.f};
         if constexpr (VEC) {
-            // beg is a multiple of 4 (part_len is), V % 4 == 0
+            // part_len and beg are multiples of 4 and V % 4 == 0; a full part
+            // is kVecPerThread float4 per thread, all loads issued up front
             const float4* z4 = reinterpret_cast<const float4*>(z);
             const int n4 = (end - beg) / 4;
             const int b4 = beg / 4;
-            int i = tid;
-            for (; i + 3 * 256 < n4; i += 4 * 256) {
-                float4 v0 = z4[b4 + i], v1 = z4[b4 + i + 256], v2 = z4[b4 + i + 512], v3 = z4[b4 + i + 768];
-                const int base = (b4 + i) * 4;
-                accum(st, v0.x, base); accum(st, v0.y, base + 1); accum(st, v0.z, base + 2); accum(st, v0.w, base + 3);
-                accum(st, v1.x, base + 1024); accum(st, v1.y, base + 1025); accum(st, v1.z, base + 1026); accum(st, v1.w, base + 1027);
-                accum(st, v2.x, base + 2048); accum(st, v2.y, base + 2049); accum(st, v2.z, base + 2050); accum(st, v2.w, base + 2051);
-                accum(st, v3.x, base + 3072); accum(st, v3.y, base + 3073); accum(st, v3.z, base + 3074); accum(st, v3.w, base + 3075);
-            }
-            for (; i < n4; i += 256) {
-                float4 v0 = z4[b4 + i];
-                const int base = (b4 + i) * 4;
-                accum(st, v0.x, base); accum(st, v0.y, base + 1); accum(st, v0.z, base + 2); accum(st, v0.w, base + 3);
+            if (n4 == kVecPerThread * 256) {
+                float4 v[kVecPerThread];
+#pragma unroll
+                for (int k = 0; k < kVecPerThread; ++k) v[k] = z4[b4 + tid + k * 256];
+                accum_vec(st, v, (b4 + tid) * 4);
+            } else {
+                for (int i = tid; i < n4; i += 256) {
+                    const float4 v1[1] = {z4[b4 + i]};
+                    accum_vec(st, v1, (b4 + i) * 4);
+                }
             }
         } else {
-            for (int i = beg + tid; i < end; i += 256) accum(st, z[i], i);
+            for (int i = beg + tid; i < end; i += 256) accum_one(st, z[i], i);
         }
         // Each thread visits its indices in increasing order, so the strict
         // '>' in accum keeps the first index of a tied maximum; merge() takes
@@ -122,18 +171,13 @@ __global__ __launch_bounds__(256) void vocab_select_commit(SelectArgs a) {
             a.part[(size_t)row * a.nparts + part] = make_float4(o.m, __int_as_float(o.a), o.s, o.t);
         }
     }
+}
 
-    if (tid == 0) {
-        __threadfence();
-        const uint32_t total = (uint32_t)a.W * a.nparts;
-        const uint32_t old = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == total - 1);
-    }
-    __syncthreads();
-    if (!s_last || wv != 0) return;
-    __threadfence();
-
-    // ---- last arrival for sequence b: commit / select / refill (one wave)
+// Commit / Eq. 11 select / refill of one sequence per 64-thread work-group
+// (one lane per slot), after vocab_stats has written every row partial.
+__global__ __launch_bounds__(64) void commit_select_refill(SelectArgs a) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
     const int W = a.W;
     const int j = lane;
     const bool in = j < W;
@@ -146,14 +190,21 @@ __global__ __launch_bounds__(256) void vocab_select_commit(SelectArgs a) {
     float H = -1.f;
     int am = -1;
     if (msk) {
+        // partials are loaded 8 at a time so their latencies overlap
         Stat o{-INFINITY, 0x7fffffff, 0.f, 0.f};
-        for (int p = 0; p < a.nparts; ++p) {
-            const float4 v = a.part[sj * a.nparts + p];
-            Stat x{v.x, __float_as_int(v.y), v.z, v.w};
-            o = merge(o, x);
+        const float4* pp = a.part + sj * a.nparts;
+        for (int p0 = 0; p0 < a.nparts; p0 += 8) {
+            float4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = p0 + q < a.nparts ? pp[p0 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const Stat x{v[q].x, __float_as_int(v[q].y), v[q].z, v[q].w};  // s == 0: empty, skipped
+                o = merge(o, x);
+            }
         }
         am = o.a;
-        H = logf(o.s) - o.t / o.s;
+        H = logf(o.s) - 0.69314718055994531f * (o.t / o.s);
     }
     const uint64_t mmask = __ballot(msk);
     bool sel = false;
@@ -194,7 +245,6 @@ __global__ __launch_bounds__(256) void vocab_select_commit(SelectArgs a) {
     if (lane == 0) {
         a.n_commit[b] = k;
         a.ctx_len[b] = L + k;
-        a.counters[b] = 0u;
     }
 }
 
@@ -203,9 +253,12 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
     const bool vec = (a.V % 4 == 0) && (a.part_len % 4 == 0) &&
                      (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0);
     if (vec)
-        hipLaunchKernelGGL(vocab_select_commit<true>, grid, block, 0, st, a);
+        hipLaunchKernelGGL(vocab_stats<true>, grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL(vocab_select_commit<false>, grid, block, 0, st, a);
+        hipLaunchKernelGGL(vocab_stats<false>, grid, block, 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(commit_select_refill, dim3((unsigned)a.B), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -34,10 +34,13 @@
  *  - Device-side checks: conditions only the data can reveal (a context
  *    length beyond the block table, a page id outside the pool, a
  *    permutation entry outside the window, non-increasing positions) are
- *    OR-ed as WEDLM_DEV_* bits into *dev_status (device int32, may be NULL);
- *    the affected sequence is skipped (no out-of-range access is made) and
- *    its outputs are zero (BAD_POS is reported only: RoPE is still applied
- *    at the given positions).  The caller reads dev_status whenever it likes.
+ *    OR-ed as WEDLM_DEV_* bits into *dev_status (device int32, may be NULL).
+ *    No out-of-range access is ever made.  BAD_CTX: the sequence is skipped
+ *    (no cache write; attention outputs zero).  BAD_PAGE: the reorder skips
+ *    that row's append; attention reads page 0 in place of the bad page, so
+ *    that sequence's outputs are meaningless.  BAD_PERM: the row is not
+ *    written.  BAD_POS is reported only (RoPE is applied at the positions
+ *    given).  The caller reads dev_status whenever it likes.
  *  - Layouts are row-major (last index fastest).  dtype WEDLM_BF16 tensors
  *    hold bfloat16 bit patterns; WEDLM_F32 tensors hold float.
  *  - KV cache: pages of page_size (= 16) tokens; k_cache and v_cache are
@@ -144,7 +147,8 @@ size_t wedlm_step_attn_workspace(const wedlm_shape *s, int32_t max_ctx_len);
  *   out    [B][W][Hq][D] device out
  *   scale  softmax scale; 0 means 1/sqrt(D)
  *   max_ctx_len  host upper bound on every ctx_len[b]; sizes the split grid
- *                (a larger ctx_len on the device is reported as BAD_CTX)
+ *                (a larger ctx_len on the device is reported as BAD_CTX);
+ *                max_ctx_len + W <= 524288 (WEDLM_ERR_UNSUPPORTED beyond)
  *   workspace / ws_bytes  device scratch of at least
  *                wedlm_step_attn_workspace(s, max_ctx_len) bytes (NULL if 0);
  *                contents need no initialisation and are not preserved
@@ -157,10 +161,9 @@ int wedlm_step_attn(const wedlm_shape *s, const void *q_phys, const void *k_cach
 
 /*
  * wedlm_select_commit_workspace -- bytes of device workspace for
- * wedlm_select_commit at (B, W, V).  The workspace must be zero-filled
- * before its first use; every completed call leaves it zero-filled again,
- * so one workspace serves any number of calls in stream order.  Two calls
- * running at the same time must not share one workspace.
+ * wedlm_select_commit at (B, W, V): one 16-byte partial per (slot, 8192
+ * logits).  Contents need no initialisation and are not preserved; calls
+ * that run at the same time must not share one workspace.
  */
 size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V);
 

@@ -1,0 +1,188 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the
+header declares, and its host-side validation and launch planning behave.
+No call here reaches a kernel launch (every case fails validation first or
+is a pure host query)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_attention_diffusion_amd as wd
+from causal_attention_diffusion_amd.binding import WedlmShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wedlm.h")
+
+OK, ERR_ARG, ERR_SHAPE, ERR_UNSUP, ERR_HIP, ERR_WS = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wedlm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_step_calls():
+    f = declared_functions()
+    for name in ["wedlm_reorder", "wedlm_step_attn", "wedlm_select_commit",
+                 "wedlm_step_attn_workspace", "wedlm_select_commit_workspace", "wedlm_last_error"]:
+        assert name in f
+
+
+def test_library_exports_every_declared_symbol():
+    lib = wd.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", wd.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (wedlm_\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = '#include "wedlm.h"\nint main(void){ wedlm_shape s; (void)s; return 0; }\n'
+    p = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I",
+                        os.path.dirname(HEADER), "-x", "c", "-"], input=src, text=True, capture_output=True)
+    assert p.returncode == 0, p.stderr
+
+
+def _shape(**kw):
+    d = dict(B=2, W=16, Hq=32, Hkv=8, D=128, page_size=16, max_pages=10, num_pages=20, dtype=1)
+    d.update(kw)
+    return WedlmShape(**d)
+
+
+NULLS = [None] * 16
+
+
+def _reorder(s):
+    lib = wd.load_library()
+    fake = C.c_void_p(0x1000)   # never dereferenced: validation fails before any launch
+    args = [fake] * 11
+    return lib.wedlm_reorder(C.byref(s) if s is not None else None, *args, 1e4, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=0), ERR_SHAPE), (dict(W=65), ERR_SHAPE), (dict(B=0), ERR_SHAPE),
+    (dict(Hq=30, Hkv=8), ERR_SHAPE), (dict(Hq=64, Hkv=2), ERR_SHAPE),
+    (dict(D=96), ERR_UNSUP), (dict(page_size=32), ERR_UNSUP),
+    (dict(dtype=5), ERR_ARG), (dict(num_pages=0), ERR_SHAPE),
+])
+def test_reorder_rejects_bad_shapes(kw, code):
+    assert _reorder(_shape(**kw)) == code
+    assert wd.wedlm_last_error() != ""
+
+
+def test_reorder_rejects_null_shape_and_pointers():
+    lib = wd.load_library()
+    assert _reorder(None) == ERR_ARG
+    s = _shape()
+    assert lib.wedlm_reorder(C.byref(s), *([None] * 11), 1e4, None, None) == ERR_ARG
+    fake = C.c_void_p(0x1000)
+    assert lib.wedlm_reorder(C.byref(s), *([fake] * 11), 0.5, None, None) == ERR_ARG   # rope_base <= 1
+
+
+def test_step_attn_validation():
+    lib = wd.load_library()
+    s = _shape(max_pages=10)
+    fake = C.c_void_p(0x1000)
+    # max_ctx_len + W beyond the block table
+    assert lib.wedlm_step_attn(C.byref(s), *([fake] * 7), 0.0, 200, None, 0, None, None) == ERR_SHAPE
+    # NULL pointer
+    assert lib.wedlm_step_attn(C.byref(s), *([None] * 7), 0.0, 100, None, 0, None, None) == ERR_ARG
+    # negative scale
+    assert lib.wedlm_step_attn(C.byref(s), *([fake] * 7), -1.0, 100, None, 0, None, None) == ERR_ARG
+    # workspace too small (this plan needs one)
+    need = lib.wedlm_step_attn_workspace(C.byref(s), 100)
+    big = _shape(max_pages=4000, B=1)
+    need_big = lib.wedlm_step_attn_workspace(C.byref(big), 60000)
+    assert need_big > 0
+    assert lib.wedlm_step_attn(C.byref(big), *([fake] * 7), 0.0, 60000, fake, need_big - 1, None,
+                               None) == ERR_WS
+    assert need >= 0
+
+
+@pytest.mark.parametrize("B,W,Hq,Hkv,D,dt,L", [
+    (4, 32, 32, 8, 128, 1, 32768), (32, 16, 32, 8, 128, 1, 8192), (1, 16, 32, 8, 128, 1, 2048),
+    (1, 8, 4, 2, 64, 0, 64), (1, 64, 32, 8, 128, 1, 300), (3, 1, 8, 8, 64, 1, 0), (2, 16, 32, 4, 128, 1, 100000), (1, 64, 32, 8, 128, 1, 524224),
+])
+def test_attention_plan_covers_every_key(B, W, Hq, Hkv, D, dt, L):
+    mp = (L + W + 15) // 16
+    ns, sk = wd.attn_plan(B, W, Hq, Hkv, D, mp, B * mp, dt, L)
+    assert ns >= 1 and sk >= 32 and sk % 32 == 0 and sk <= 8192
+    assert ns * sk >= L + W                 # the grid covers every visible key
+    assert (ns - 1) * sk < L + W            # and no split is wholly past the end
+    s = _shape(B=B, W=W, Hq=Hq, Hkv=Hkv, D=D, max_pages=mp, num_pages=B * mp, dtype=dt)
+    ws = wd.load_library().wedlm_step_attn_workspace(C.byref(s), L)
+    assert (ws == 0) == (ns == 1)
+
+
+def test_split_override_validation():
+    with pytest.raises(wd.WedlmError):
+        wd.wedlm_set_attn_split_keys(100)
+    with pytest.raises(wd.WedlmError):
+        wd.wedlm_set_attn_split_keys(16384)
+    wd.wedlm_set_attn_split_keys(128)
+    try:
+        ns, sk = wd.attn_plan(1, 16, 32, 8, 128, 200, 200, 1, 3000)
+        assert sk == 128 and ns == (3000 + 16 + 127) // 128
+    finally:
+        wd.wedlm_set_attn_split_keys(0)
+
+
+def test_select_commit_validation_and_workspace():
+    lib = wd.load_library()
+    fake = C.c_void_p(0x1000)
+    assert lib.wedlm_select_commit(0, 16, 100, *([fake] * 9), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_SHAPE
+    assert lib.wedlm_select_commit(2, 65, 100, *([fake] * 9), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_SHAPE
+    assert lib.wedlm_select_commit(2, 16, 100, *([None] * 9), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_ARG
+    assert lib.wedlm_select_commit(2, 16, 100, *([fake] * 9), float("nan"), 1.0, 100, fake, 1 << 20,
+                                   None) == ERR_ARG
+    need = lib.wedlm_select_commit_workspace(64, 16, 151936)
+    assert need >= 64 * 16 * 19 * 16      # one float4 per (slot, 8192 logits)
+    assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 9), 0.1, 1.0, 100, fake, need - 1,
+                                   None) == ERR_WS
+    assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 9), 0.1, 1.0, 100, None, need, None) == ERR_WS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros((1, 8, 4, 64))
+    kc = torch.zeros((5, 2, 16, 64))
+    bt = torch.zeros((1, 5), dtype=torch.int32)
+    with pytest.raises(wd.WedlmError):
+        wd.wedlm_step_attn(x, kc, kc, bt, torch.zeros(1, dtype=torch.int32),
+                           torch.zeros((1, 8), dtype=torch.int32), x.clone(), max_ctx_len=10)
+
+
+def test_binding_checks_shapes_before_pointers():
+    import torch
+    x = torch.zeros((1, 8, 4, 64))
+    kc = torch.zeros((5, 2, 16, 64))
+    bt = torch.zeros((1, 5), dtype=torch.int32)
+    with pytest.raises(wd.WedlmError, match="perm"):
+        wd.wedlm_step_attn(x, kc, kc, bt, torch.zeros(1, dtype=torch.int32),
+                           torch.zeros((1, 7), dtype=torch.int32), x.clone(), max_ctx_len=10)
+    with pytest.raises(wd.WedlmError, match="cache"):
+        wd.wedlm_step_attn(x, torch.zeros((5, 2, 8, 64)), kc, bt, torch.zeros(1, dtype=torch.int32),
+                           torch.zeros((1, 8), dtype=torch.int32), x.clone(), max_ctx_len=10)
+
+
+def test_product_and_oracle_share_no_code():
+    """The HIP path never imports the oracle, and the oracle never imports the
+    product package; only the input generator module is shared."""
+    pkg = os.path.join(ROOT, "causal_attention_diffusion_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "wedlm_oracle" not in text, f
+                assert "workloads" not in text or f.endswith(".md"), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "causal_attention_diffusion_amd" not in text, f
+            assert not re.search(r'#include\s+"[^"]*(csrc|include/wedlm)', text), f

@@ -135,6 +135,7 @@ def test_attention_parity(name, n_rows, dev):
     cfg = wl.CONFIGS[name]
     print(f"[attn] {name}", flush=True)
     err, status = _attn_alone(cfg, dev, n_rows)
+    print(f"[attn] {name}: max|gpu-oracle|/max|oracle| = {err:.3e} (tol {ATTN_TOL[cfg.dtype]})")
     assert status == 0
     assert err <= ATTN_TOL[cfg.dtype], err
 
@@ -155,6 +156,7 @@ def test_decode_step_parity(name, n_rows, dev):
     ref = oracle.decode_step_attention(inp, rows=rows)
     got = wl.torch_storage_to_f64(t["out"], cfg.dtype)
     err = rel_err(got, ref["out"]) if rows is None else compare_rows(got, ref["out"], rows, ref["perm"])
+    print(f"[step] {name}: max|gpu-oracle|/max|oracle| = {err:.3e} (tol {ATTN_TOL[cfg.dtype]})")
     assert err <= ATTN_TOL[cfg.dtype], err
 
 
@@ -183,6 +185,7 @@ def test_edge_cases(label, over, split, dev):
     wd.wedlm_set_attn_split_keys(split)
     try:
         err, status = _attn_alone(cfg, dev)
+        print(f"[edge] {label}: attention err {err:.3e}")
         assert status == 0
         assert err <= ATTN_TOL[cfg.dtype], err
         inp = wl.make_attn_inputs(cfg)
