@@ -77,6 +77,19 @@ extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const 
 
 // ---------------------------------------------------------------- attention plan
 static int32_t g_split_override = 0;
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 static const int64_t kMaxContext = 64ll * kMaxSplitPages * kPage;  // 524288 keys incl. the window
 
 struct Plan {
@@ -98,14 +111,14 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     if (g_split_override > 0) {
         sk = g_split_override;
     } else {
-        // aim at ~2 resident work-groups per CU over 256 CUs, but keep the
-        // fp32 partials (RT*D*4 bytes per split) small next to the KV bytes
-        // a split streams: at least 8 keys per row of the tile, >= 128 keys
-        const int64_t target = 512;
+        // One round of work-groups over the device (a bf16 work-group fills a
+        // CU's LDS): the key work of every (sequence, KV head, row tile) at
+        // the bound is cut so that the splits number about one per CU.  At
+        // least 256 keys per split so the per-split prologue and the fp32
+        // partial (RT*D*4 bytes) stay small next to the K/V a split streams.
+        const int64_t target = device_cus();
         sk = (T * pairs + target - 1) / target;
-        int64_t lo = (int64_t)p.RT * 8;
-        if (lo < 128) lo = 128;
-        if (sk < lo) sk = lo;
+        if (sk < 256) sk = 256;
     }
     sk = (sk + p.chunk - 1) / p.chunk * p.chunk;
     if (sk > (int64_t)kMaxSplitPages * kPage) sk = (int64_t)kMaxSplitPages * kPage;

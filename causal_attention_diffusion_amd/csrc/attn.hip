@@ -84,8 +84,13 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
     const int hl = lane >> 5;   // lane half
     const int col = lane & 31;  // row within the wave's 32 (S^T / O^T column)
 
-    const int pid = blockIdx.x / a.nsplit;
-    const int split = blockIdx.x - pid * a.nsplit;
+    // split-major order: every (sequence, KV head, row tile) gets its first
+    // split dispatched before any second split, so the dispatcher hands the
+    // remaining (equal-size) splits of long sequences to whichever CU frees
+    // up first
+    const int npid = a.B * a.Hkv * a.row_tiles;
+    const int split = blockIdx.x / npid;
+    const int pid = blockIdx.x - split * npid;
     const int rt = pid % a.row_tiles;
     const int bk = pid / a.row_tiles;
     const int kvh = bk % a.Hkv;
