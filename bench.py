@@ -34,6 +34,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Counter-derived HBM bytes per attention launch, written from two rocprofv3
+# --pmc passes (FETCH_SIZE, WRITE_SIZE) over this same command and scaled by a
+# plain-copy calibration.  Used only while the attention sources still hash to
+# the value recorded there and the run is the one profiled.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long_b4.md")
+ATTN_SOURCES = ["attn_bf16.hip", "attn.hip", "api.hip", "kernels.hpp", "common.hpp"]
 METRIC = "window tokens/sec and decode steps/sec per GPU; attn achieved HBM GB/s vs peak"
 
 
@@ -219,13 +225,43 @@ def main():
                           "masked_rows_per_step_in_stream": float(masked_rows.mean())},
         "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args),
                      "kernel": "wedlm_step_attn (attn_split + attn_combine)"},
     }
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, args, inp)
     print(json.dumps(result), flush=True)
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "causal_attention_diffusion_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(args):
+    """Bytes per attention launch from the committed counter summary, or None
+    when the kernel sources or the run differ from the profiled ones."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line[2:].split(": ", 1) for line in fh.read().splitlines()
+                      if line.startswith("- ") and ": " in line)
+    except OSError:
+        return None
+    run = {"workload": args.workload, "steps": str(args.steps), "warmup": str(args.warmup),
+           "vocab": str(args.vocab), "split_keys": str(args.split_keys)}
+    if kv.get("source_sha256", "").strip("` ") != attn_source_hash():
+        return None
+    if any(kv.get(k, "").strip("` ") != v for k, v in run.items()):
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"].strip("` "))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, args, inp):
@@ -246,17 +282,22 @@ def cpu_baseline(cfg, args, inp):
                            steps=0, kind="mixture")
     lg = wl.make_logits_np(scfg, 0)
     tok = np.where(inp.filled[sel] == 1, 1, args.vocab).astype(np.int32)
-    t0 = time.perf_counter()
-    perm, qp, kw, vw = oracle.reorder(inp.filled[sel], inp.pos[sel], q, k, v, dt, cfg.rope_base)
-    dk = [np.concatenate([pk[i], kw[i]], 0) for i in range(nseq)]
-    dv = [np.concatenate([pv[i], vw[i]], 0) for i in range(nseq)]
-    oracle.attention(qp, dk, dv, inp.ctx_len[sel], perm)
-    oracle.select_commit(lg, tok, inp.filled[sel], inp.pos[sel], inp.ctx_len[sel], 0.25, 9.0, args.vocab)
-    dt_s = time.perf_counter() - t0
-    return {"value": round(nseq * cfg.W / dt_s, 3), "unit": "window tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    # the same step repeated until about 10 s of CPU work (at most 4 times)
+    reps, dt_s = 0, 0.0
+    while reps < 4 and dt_s < 10.0:
+        t0 = time.perf_counter()
+        perm, qp, kw, vw = oracle.reorder(inp.filled[sel], inp.pos[sel], q, k, v, dt, cfg.rope_base)
+        dk = [np.concatenate([pk[i], kw[i]], 0) for i in range(nseq)]
+        dv = [np.concatenate([pv[i], vw[i]], 0) for i in range(nseq)]
+        oracle.attention(qp, dk, dv, inp.ctx_len[sel], perm)
+        oracle.select_commit(lg, tok, inp.filled[sel], inp.pos[sel], inp.ctx_len[sel], 0.25, 9.0, args.vocab)
+        dt_s += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(reps * nseq * cfg.W / dt_s, 3), "unit": "window tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{nseq} of {cfg.B} sequences, one full step (reorder, all {cfg.W * cfg.Hq} "
-                      f"attention rows per sequence, select/commit over V={args.vocab}); {dt_s:.2f} s"}
+                      f"attention rows per sequence, select/commit over V={args.vocab}) repeated "
+                      f"{reps}x; {dt_s:.2f} s"}
 
 
 if __name__ == "__main__":
