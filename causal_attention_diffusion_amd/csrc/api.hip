@@ -199,7 +199,7 @@ extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const v
 }
 
 // ---------------------------------------------------------------- select / commit
-static const int kPartLen = 8192;  // logits per work-group: 256 threads x 8 float4
+static const int kPartLen = 16384;  // logits per work-group: 256 threads x 16 float4
 
 static void select_plan(int32_t V, int* nparts, int* part_len) {
     int pl = kPartLen;

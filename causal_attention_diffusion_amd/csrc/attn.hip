@@ -339,76 +339,71 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
     }
 }
 
-// Merge the split partials of every (b, g, row) and scatter the rows to
-// logical slot order.  A work-group takes 256 / (D/4) rows; a thread owns 4
-// consecutive d of one row (16-byte loads of the fp32 partials).  The split
-// weights 2^(m_s - M) and the merged denominator are computed once per row
-// into LDS; the split loop is unrolled by 4 so the partial loads overlap.
+// Merge the split partials of every (b, g, row) by the log-sum-exp rule and
+// scatter the rows to logical slot order.  A thread owns 4 consecutive d of
+// one row.  It loads the (m, l) of its row's splits and its 16-byte slices of
+// the fp32 partials in batches of 8 splits, all issued before any is used,
+// so one memory latency covers a batch (the D/4 threads of a row read the
+// same (m, l) words: one request per wave).  No LDS, no barrier.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     constexpr int D4 = D / 4;
     constexpr int RPB = 256 / D4;
-    constexpr int MAXS = 64;                   // splits handled in LDS at once
-    __shared__ float s_w[RPB][MAXS];
-    __shared__ float s_inv[RPB];
+    constexpr int SB = 8;                      // splits per batch
     const int tid = threadIdx.x;
     const int lr = tid / D4;
     const int d = (tid % D4) * 4;
     const long row = (long)blockIdx.x * RPB + lr;
     const int npid = a.B * a.Hkv * a.row_tiles;
     const int pid = (int)(row / a.RT);
+    if (pid >= npid) return;
     const int m_loc = (int)(row - (long)pid * a.RT);
-    const bool live = pid < npid;
-    int b = 0, kvh = 0, m = 0, nvalid = 0;
-    if (live) {
-        const int rt = pid % a.row_tiles;
-        const int bk = pid / a.row_tiles;
-        kvh = bk % a.Hkv;
-        b = bk / a.Hkv;
-        m = rt * a.RT + m_loc;
-        const int L = a.ctx_len[b];
-        const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
-        const int T_len = ctx_ok ? L + a.W : 0;
-        nvalid = min(a.nsplit, (T_len + a.split_keys - 1) / a.split_keys);
-    }
-    const size_t base = live ? (size_t)pid * a.nsplit * a.RT + m_loc : 0;
-    // one thread per row computes the weights
-    if (tid % D4 == 0) {
-        float M = -INFINITY;
-        for (int s = 0; s < nvalid; ++s) M = fmaxf(M, a.part_ml[base + (size_t)s * a.RT].x);
-        float den = 0.f;
-        for (int s = 0; s < nvalid && s < MAXS; ++s) {
-            const float2 ml = a.part_ml[base + (size_t)s * a.RT];
-            const float w = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-            s_w[lr][s] = w;
-            den += w * ml.y;
-        }
-        s_inv[lr] = den > 0.f ? 1.f / den : 0.f;
-    }
-    __syncthreads();
-    if (!live || m >= a.M) return;
-    const int ns = nvalid < MAXS ? nvalid : MAXS;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int rt = pid % a.row_tiles;
+    const int bk = pid / a.row_tiles;
+    const int kvh = bk % a.Hkv;
+    const int b = bk / a.Hkv;
+    const int m = rt * a.RT + m_loc;
+    if (m >= a.M) return;
+    const int L = a.ctx_len[b];
+    const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
+    const int T_len = ctx_ok ? L + a.W : 0;
+    const int nvalid = min(a.nsplit, (T_len + a.split_keys - 1) / a.split_keys);
+    const size_t base = (size_t)pid * a.nsplit * a.RT + m_loc;
     const float* po = a.part_o + base * D + d;
     const size_t stride = (size_t)a.RT * D;
-    int s = 0;
-    for (; s + 4 <= ns; s += 4) {
-        const float4 v0 = *reinterpret_cast<const float4*>(po + (s + 0) * stride);
-        const float4 v1 = *reinterpret_cast<const float4*>(po + (s + 1) * stride);
-        const float4 v2 = *reinterpret_cast<const float4*>(po + (s + 2) * stride);
-        const float4 v3 = *reinterpret_cast<const float4*>(po + (s + 3) * stride);
-        const float w0 = s_w[lr][s], w1 = s_w[lr][s + 1], w2 = s_w[lr][s + 2], w3 = s_w[lr][s + 3];
-        acc.x += w0 * v0.x + w1 * v1.x + w2 * v2.x + w3 * v3.x;
-        acc.y += w0 * v0.y + w1 * v1.y + w2 * v2.y + w3 * v3.y;
-        acc.z += w0 * v0.z + w1 * v1.z + w2 * v2.z + w3 * v3.z;
-        acc.w += w0 * v0.w + w1 * v1.w + w2 * v2.w + w3 * v3.w;
+
+    float M = -INFINITY, den = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < nvalid; s0 += SB) {
+        float2 ml[SB];
+        float4 v[SB];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const int s = s0 + j;
+            if (s < nvalid) {
+                ml[j] = a.part_ml[base + (size_t)s * a.RT];
+                v[j] = *reinterpret_cast<const float4*>(po + s * stride);
+            } else {
+                ml[j] = make_float2(-INFINITY, 0.f);
+                v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float Mb = M;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) Mb = fmaxf(Mb, ml[j].x);
+        if (Mb == -INFINITY) continue;         // nothing visible yet
+        const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+        den *= c;
+        acc.x *= c; acc.y *= c; acc.z *= c; acc.w *= c;
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            const float w = __builtin_amdgcn_exp2f(ml[j].x - Mb);   // 0 for empty splits
+            den += w * ml[j].y;
+            acc.x += w * v[j].x; acc.y += w * v[j].y; acc.z += w * v[j].z; acc.w += w * v[j].w;
+        }
+        M = Mb;
     }
-    for (; s < ns; ++s) {
-        const float4 v0 = *reinterpret_cast<const float4*>(po + s * stride);
-        const float w0 = s_w[lr][s];
-        acc.x += w0 * v0.x; acc.y += w0 * v0.y; acc.z += w0 * v0.z; acc.w += w0 * v0.w;
-    }
-    const float inv = s_inv[lr];
+    const float inv = den > 0.f ? 1.f / den : 0.f;
     const int r = m / a.G;
     const int h = kvh * a.G + m % a.G;
     const int slot = a.perm[(size_t)b * a.W + r];
@@ -417,10 +412,14 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
         return;
     }
     T* o = static_cast<T*>(a.out) + (((size_t)b * a.W + slot) * a.Hq + h) * D + d;
-    DT<T>::store(o, 0, acc.x * inv);
-    DT<T>::store(o, 1, acc.y * inv);
-    DT<T>::store(o, 2, acc.z * inv);
-    DT<T>::store(o, 3, acc.w * inv);
+    if constexpr (sizeof(T) == 2) {
+        uint2 pk;
+        pk.x = f32_to_bf16(acc.x * inv) | ((uint32_t)f32_to_bf16(acc.y * inv) << 16);
+        pk.y = f32_to_bf16(acc.z * inv) | ((uint32_t)f32_to_bf16(acc.w * inv) << 16);
+        *reinterpret_cast<uint2*>(o) = pk;
+    } else {
+        *reinterpret_cast<float4*>(o) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
 }
 
 template <typename T, int D>

@@ -7,12 +7,13 @@
 // their logical positions) and "Method" (inference paragraph: the window is
 // reordered with filled tokens first before the causal pass on the cache).
 //
-// One work-group per (physical row r, sequence b).  Each wave derives the
-// permutation with two ballots (filled / masked masks) and a prefix
-// popcount: slot i lands at physical row popc(filled below i) if filled,
-// else n_obs + popc(masked below i).  The work-group then rotates the Hq
-// query heads and Hkv key heads of that slot at its logical position and
-// writes the key/value rows into the paged cache at token ctx_len[b] + r.
+// One work-group per (logical slot i, sequence b).  It loads the rows of
+// slot i at once, and meanwhile each wave derives the slot's physical row
+// with two ballots (filled / masked masks) and a prefix popcount: slot i
+// lands at r = popc(filled below i) if filled, else n_obs + popc(masked
+// below i).  The work-group then rotates the Hq query heads and Hkv key
+// heads at the slot's logical position into physical row r and writes the
+// key/value rows into the paged cache at token ctx_len[b] + r.
 // The work is tiny (B*W*(Hq+2Hkv)*D elements) and latency-bound; angles and
 // rotations are float64 so that positions up to 2^31 keep full accuracy.
 #include "kernels.hpp"
@@ -20,48 +21,139 @@
 namespace wedlm {
 
 
+// 4 consecutive elements (8-byte bf16 / 16-byte fp32 access; the offsets
+// used here are multiples of 4 elements, so the accesses are aligned)
+__device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float (&x)[4]) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
+    x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
+}
+__device__ __forceinline__ void store4(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store4(bf16_t* p, const float (&x)[4]) {
+    uint2 v;
+    v.x = f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    v.y = f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
-    const int r = blockIdx.x;
+    const int i = blockIdx.x;   // logical slot
     const int b = blockIdx.y;
     const int W = a.W, D = a.D, half = D / 2;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
 
-    // Every wave derives the permutation entry of row r by itself: no LDS,
-    // no barrier, and the loads below overlap.
+    // Work items are 4 consecutive pairs (c .. c+3 with c+D/2 .. c+D/2+3) of
+    // one head: Hq query heads, then Hkv key heads; value rows are copied in
+    // 4-element pieces.  The rows of slot i depend on nothing else, so the
+    // first batch of loads is issued before the permutation, the page and the
+    // angle table are known.
+    constexpr int kMaxItems = 4;
+    const int qn = a.Hq * (half / 4), kn = a.Hkv * (half / 4), vn = a.Hkv * (D / 4);
+    const int n_all = qn + kn + vn;
+    const T* qs = static_cast<const T*>(a.q) + ((size_t)b * W + i) * a.Hq * D;
+    const T* ks = static_cast<const T*>(a.k) + ((size_t)b * W + i) * a.Hkv * D;
+    const T* vs = static_cast<const T*>(a.v) + ((size_t)b * W + i) * a.Hkv * D;
+    float x0[kMaxItems][4], x1[kMaxItems][4];
+    auto load_items = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < kMaxItems; ++u) {
+            const int it = base + u * 256;
+            if (it >= n_all) continue;
+            if (it < qn + kn) {
+                const bool isq = it < qn;
+                const int j = isq ? it : it - qn;
+                const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
+                const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
+                load4(src, x0[u]);
+                load4(src + half, x1[u]);
+            } else {
+                const int j = it - qn - kn;
+                load4(vs + (size_t)j * 4, x0[u]);
+            }
+        }
+    };
+
+    load_items(tid);
+
+    // Every wave derives the physical row of slot i by itself from two
+    // ballots and a prefix popcount: no LDS, no barrier.
     const bool in = lane < W;
     const int f = in ? a.filled[(size_t)b * W + lane] : 0;
     const int p_lane = in ? a.pos[(size_t)b * W + lane] : 0;
     const int L = a.ctx_len[b];
     const uint64_t fm = __ballot(in && f != 0);
     const uint64_t mm = __ballot(in && f == 0);
-    const uint64_t below = lane == 0 ? 0ull : ((1ull << lane) - 1ull);
+    const uint64_t below = i == 0 ? 0ull : ((1ull << i) - 1ull);
     const int n_obs = __popcll(fm);
-    const int phys = f ? __popcll(fm & below) : n_obs + __popcll(mm & below);
-    const uint64_t hit = __ballot(in && phys == r);
-    const int slot = (int)__builtin_ctzll(hit);   // the map slot -> phys is a bijection onto [0, W)
-    const int p = __shfl(p_lane, slot);
+    const int r = ((fm >> i) & 1ull) ? __popcll(fm & below) : n_obs + __popcll(mm & below);
+    const int p = __shfl(p_lane, i);
 
+    // The window's tokens L .. L+W-1 span at most W/16 + 2 pages: their
+    // block-table entries are read as soon as L is known, one per lane.
     const bool ctx_ok = L >= 0 && (int64_t)L + W <= (int64_t)a.max_pages * kPage;
     int page = -1;
-    if (ctx_ok) {
-        page = a.block_table[(size_t)b * a.max_pages + (L + r) / kPage];
-        if (page < 0 || page >= a.num_pages) page = -1;
+    {
+        const int fp = ctx_ok ? L / kPage : 0;
+        const int npg = ctx_ok ? (L + W - 1) / kPage - fp + 1 : 0;
+        const int pg_lane = lane < npg ? a.block_table[(size_t)b * a.max_pages + fp + lane] : -1;
+        if (ctx_ok) {
+            page = __shfl(pg_lane, (L + r) / kPage - fp);
+            if (page < 0 || page >= a.num_pages) page = -1;
+        }
     }
     if (tid == 0) {
-        a.perm[(size_t)b * W + r] = slot;
+        a.perm[(size_t)b * W + r] = i;
         if (!ctx_ok) set_status(a.status, WEDLM_DEV_BAD_CTX);
         else if (page < 0) set_status(a.status, WEDLM_DEV_BAD_PAGE);
     }
-    if (tid < 64 && r == 0) {
+    if (tid < 64 && i == 0) {
         const int p_prev = __shfl_up(p_lane, 1);
         const bool bad_pos = in && (p_lane < 0 || (lane > 0 && p_lane <= p_prev));
         if (__ballot(bad_pos) && lane == 0) set_status(a.status, WEDLM_DEV_BAD_POS);
     }
+    const int t_row = L + r;
+    const size_t row0 = page >= 0 ? ((size_t)page * a.Hkv) * kPage + (t_row % kPage) : 0;
+    T* qd = static_cast<T*>(a.q_phys) + ((size_t)b * W + r) * a.Hq * D;
+    T* kc = static_cast<T*>(a.k_cache);
+    T* vc = static_cast<T*>(a.v_cache);
 
     // cos/sin of the D/2 pair angles, float64, once per work-group
     __shared__ double s_cs[64], s_sn[64];
+    auto store_items = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < kMaxItems; ++u) {
+            const int it = base + u * 256;
+            if (it >= n_all || (it >= qn && page < 0)) continue;   // no cache row without a page
+            if (it < qn + kn) {
+                const bool isq = it < qn;
+                const int j = isq ? it : it - qn;
+                const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
+                T* dst = isq ? qd + (size_t)hh * D + c : kc + (row0 + (size_t)hh * kPage) * D + c;
+                float y0[4], y1[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const double cs = s_cs[c + e], sn = s_sn[c + e];
+                    y0[e] = (float)((double)x0[u][e] * cs - (double)x1[u][e] * sn);
+                    y1[e] = (float)((double)x1[u][e] * cs + (double)x0[u][e] * sn);
+                }
+                store4(dst, y0);
+                store4(dst + half, y1);
+            } else {
+                const int j = it - qn - kn;
+                const int g = j / (D / 4), d = (j % (D / 4)) * 4;
+                store4(vc + (row0 + (size_t)g * kPage) * D + d, x0[u]);
+            }
+        }
+    };
+
     if (tid < half) {
         double sn, cs;
         sincos((double)p * exp2(-(2.0 * tid / D) * a.log2_base), &sn, &cs);
@@ -69,70 +161,10 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
         s_sn[tid] = sn;
     }
     __syncthreads();
-
-    // Work items are 4 consecutive pairs (c .. c+3 with c+D/2 .. c+D/2+3) of
-    // one head: Hq query heads, then Hkv key heads; value rows are copied in
-    // 4-element pieces.  Each thread loads all of its items before it
-    // computes, so the loads overlap.
-    constexpr int kMaxItems = 4;
-    const int qn = a.Hq * (half / 4), kn = a.Hkv * (half / 4), vn = a.Hkv * (D / 4);
-    const int t_row = L + r;
-    const size_t row0 = page >= 0 ? ((size_t)page * a.Hkv) * kPage + (t_row % kPage) : 0;
-    const T* qs = static_cast<const T*>(a.q) + ((size_t)b * W + slot) * a.Hq * D;
-    T* qd = static_cast<T*>(a.q_phys) + ((size_t)b * W + r) * a.Hq * D;
-    const T* ks = static_cast<const T*>(a.k) + ((size_t)b * W + slot) * a.Hkv * D;
-    const T* vs = static_cast<const T*>(a.v) + ((size_t)b * W + slot) * a.Hkv * D;
-    T* kc = static_cast<T*>(a.k_cache);
-    T* vc = static_cast<T*>(a.v_cache);
-    const int n_items = qn + (page >= 0 ? kn + vn : 0);
-    for (int base = tid; base < n_items; base += kMaxItems * 256) {
-        float x0[kMaxItems][4], x1[kMaxItems][4];
-#pragma unroll
-        for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * 256;
-            if (it >= n_items) continue;
-            if (it < qn + kn) {
-                const bool isq = it < qn;
-                const int j = isq ? it : it - qn;
-                const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-                const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x0[u][e] = DT<T>::load(src, e);
-                    x1[u][e] = DT<T>::load(src, e + half);
-                }
-            } else {
-                const int j = it - qn - kn;
-                const T* src = vs + (size_t)j * 4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x0[u][e] = DT<T>::load(src, e);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * 256;
-            if (it >= n_items) continue;
-            if (it < qn + kn) {
-                const bool isq = it < qn;
-                const int j = isq ? it : it - qn;
-                const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-                T* dst = isq ? qd + (size_t)hh * D + c : kc + (row0 + (size_t)hh * kPage) * D + c;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double cs = s_cs[c + e], sn = s_sn[c + e];
-                    const double y0 = (double)x0[u][e] * cs - (double)x1[u][e] * sn;
-                    const double y1 = (double)x1[u][e] * cs + (double)x0[u][e] * sn;
-                    DT<T>::store(dst, e, (float)y0);
-                    DT<T>::store(dst, e + half, (float)y1);
-                }
-            } else {
-                const int j = it - qn - kn;
-                const int g = j / (D / 4), d = (j % (D / 4)) * 4;
-                T* dst = vc + (row0 + (size_t)g * kPage) * D + d;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) DT<T>::store(dst, e, x0[u][e]);
-            }
-        }
+    store_items(tid);
+    for (int base = tid + kMaxItems * 256; base < n_all; base += kMaxItems * 256) {
+        load_items(base);
+        store_items(base);
     }
 }
 

@@ -13,7 +13,7 @@
 // Two launches.  vocab_stats: work-group (b, j, part) streams part `part` of
 // the logits row of slot j when that slot is masked (rows of filled slots
 // are never read): per thread an online (max, first argmax, S = sum 2^u,
-// T = sum u 2^u with u = (z - max) log2 e) over 16-byte loads issued 8 at a
+// T = sum u 2^u with u = (z - max) log2 e) over 16-byte loads issued 16 at a
 // time, then a wave/LDS merge, and the row-part partial goes to the
 // workspace.  commit_select_refill: one wave per sequence, one lane per
 // slot, merges its rows' partials (H = ln S - ln2 T/S) and runs commit /
@@ -25,7 +25,7 @@
 
 namespace wedlm {
 
-constexpr int kVecPerThread = 8;  // float4 loads per thread per full part
+constexpr int kVecPerThread = 16;  // float4 loads per thread per full part (all in flight together)
 
 
 // Online statistics of a logits row slice: max m, first argmax a,

@@ -161,7 +161,7 @@ int wedlm_step_attn(const wedlm_shape *s, const void *q_phys, const void *k_cach
 
 /*
  * wedlm_select_commit_workspace -- bytes of device workspace for
- * wedlm_select_commit at (B, W, V): one 16-byte partial per (slot, 8192
+ * wedlm_select_commit at (B, W, V): one 16-byte partial per (slot, 16384
  * logits).  Contents need no initialisation and are not preserved; calls
  * that run at the same time must not share one workspace.
  */

@@ -141,7 +141,7 @@ def test_select_commit_validation_and_workspace():
     assert lib.wedlm_select_commit(2, 16, 100, *([fake] * 9), float("nan"), 1.0, 100, fake, 1 << 20,
                                    None) == ERR_ARG
     need = lib.wedlm_select_commit_workspace(64, 16, 151936)
-    assert need >= 64 * 16 * 19 * 16      # one float4 per (slot, 8192 logits)
+    assert need >= 64 * 16 * 10 * 16      # one float4 per (slot, 16384 logits)
     assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 9), 0.1, 1.0, 100, fake, need - 1,
                                    None) == ERR_WS
     assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 9), 0.1, 1.0, 100, None, need, None) == ERR_WS
