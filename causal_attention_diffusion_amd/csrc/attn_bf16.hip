@@ -11,9 +11,9 @@
 //
 // What differs from the fp32 kernel (attn.hip) is how K/V reach LDS:
 //  * global_load_lds_dwordx4 writes each wave's 16-byte loads straight into
-//    LDS (1 KB per wave instruction), so no VGPRs hold data in flight and an
-//    NST-stage ring of 64-key chunks keeps NST-1 chunks (96 KB at D = 128)
-//    in flight per work-group;
+//    LDS (1 KB per wave instruction), so no VGPRs hold data in flight; rings
+//    of 64-key stages keep AHEAD stages (96 KB at D = 128) in flight per
+//    work-group;
 //  * completion is tracked per wave with s_waitcnt vmcnt(n) and made visible
 //    to the other waves by one s_barrier per chunk;
 //  * LDS rows are unpadded; 16-byte chunks are XOR-swizzled per key (the
@@ -36,8 +36,14 @@ struct Bf16Cfg {
     static constexpr int NT = 64 * NWAVES;
     static constexpr int SK = 64;                    // keys per stage
     static constexpr int RC = D * 2 / 16;            // 16-byte chunks per key row (8 or 16)
-    static constexpr int NST = D == 128 ? 4 : 8;     // ring stages
-    static constexpr int KBYTES = SK * D * 2;        // K bytes per stage
+    // DMA runs AHEAD stages in front of the stage being computed.  K of
+    // stage st is last read in iteration st, V in iteration st+1 (its PV
+    // trails by one), so the K ring has AHEAD+1 slots and the V ring AHEAD+2:
+    // 144 KB at D = 128 (3 stages = 96 KB in flight), 136 KB at D = 64.
+    static constexpr int AHEAD = D == 128 ? 3 : 7;
+    static constexpr int NKS = AHEAD + 1;
+    static constexpr int NVS = AHEAD + 2;
+    static constexpr int KBYTES = SK * D * 2;        // K (or V) bytes per stage
     static constexpr int STAGE = 2 * KBYTES;         // K then V
     static constexpr int LPS = STAGE / 1024 / NWAVES; // DMA instructions per wave per stage
     static constexpr int NDT = D / 32;
@@ -84,38 +90,52 @@ __device__ __forceinline__ void wait_stage(int ahead) {
     }
 }
 
-// Transpose reads of V for one 16-key MFMA k-step, all d-tiles at once:
-// rows key0 (+ OFF) and key0 + 8 (+ OFF + 8 rows) of each d-tile address.
+// Transpose reads of V for one 32-key tile, all d-tiles, both 16-key
+// k-steps: rows key0 and key0 + 8 (k-step 0), key0 + 16 and key0 + 24
+// (k-step 1) of each d-tile address; r[kk * 2 NDT + half * NDT + dt].
 // Issued from inline asm with their own lgkmcnt wait: the compiler's wait
 // insertion would otherwise put an s_waitcnt vmcnt(0) in front of every
 // ds_read_b64_tr_b16 (it cannot tell them apart from the in-flight DMA
 // writes of later stages), which would drain the prefetch ring.
-template <int OFF, int ROWB>
-__device__ __forceinline__ void tr_reads4(const uint32_t (&ad)[4], s16x4 (&lo)[4], s16x4 (&hi)[4]) {
+template <int ROWB>
+__device__ __forceinline__ void tr_tile4(const uint32_t (&ad)[4], s16x4 (&r)[16]) {
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %18\n\t"
+        "ds_read_b64_tr_b16 %3, %19\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %14, %18 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:%22\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
-          "=&v"(hi[3])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(OFF), "i"(OFF + 8 * ROWB));
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(8 * ROWB), "i"(16 * ROWB), "i"(24 * ROWB));
 }
-template <int OFF, int ROWB>
-__device__ __forceinline__ void tr_reads2(const uint32_t (&ad)[2], s16x4 (&lo)[2], s16x4 (&hi)[2]) {
+template <int ROWB>
+__device__ __forceinline__ void tr_tile2(const uint32_t (&ad)[2], s16x4 (&r)[8]) {
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
-        "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(hi[0]), "=&v"(hi[1])
-        : "v"(ad[0]), "v"(ad[1]), "i"(OFF), "i"(OFF + 8 * ROWB));
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(ad[0]), "v"(ad[1]), "i"(8 * ROWB), "i"(16 * ROWB), "i"(24 * ROWB));
 }
 
 // Value of lane l ^ 32 (v_permlane32_swap: the upper half of the first
@@ -135,7 +155,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     constexpr int NKG = C::NWAVES / NRG;
     constexpr int RT = 32 * NRG;
     constexpr int MSTRIDE = D + 4;                              // merge rows, floats
-    constexpr int RING = C::NST * C::STAGE;              // NST slots of (K, V)
+    constexpr int RING = (C::NKS + C::NVS) * C::KBYTES;  // K ring, then V ring
     constexpr int MERGE = NKG * RT * MSTRIDE * 4;
     constexpr int SMEM = RING > MERGE ? RING : MERGE;
     __shared__ __attribute__((aligned(1024))) char s_ring[SMEM];
@@ -217,7 +237,8 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 
     // DMA plan.  A stage is 4 pages of K and 4 pages of V (64 keys, one
     // (page, head) block each).  Wave w loads one whole block per stage:
-    // waves 0..3 the K pages, waves 4..7 the V pages of ring slot st % NST.
+    // waves 0..3 the K pages into K slot st % NKS, waves 4..7 the V pages
+    // into V slot st % NVS.
     // The lane offsets inside a block (row,
     // swizzled chunk) never change, so a stage costs one page-table read per
     // wave and LPS loads with a uniform base.
@@ -237,8 +258,8 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         lane_off[n] = (uint32_t)(kin * ROWB + c * 16);
     }
     static_assert(C::LPS * KPB == kPage, "one wave loads exactly one page block per stage");
-    auto kslot = [&](int st) { return s_ring + (st % C::NST) * C::STAGE; };
-    auto vslot = [&](int st) { return kslot(st) + C::KBYTES; };
+    auto kslot = [&](int st) { return s_ring + (st % C::NKS) * C::KBYTES; };
+    auto vslot = [&](int st) { return s_ring + (C::NKS + st % C::NVS) * C::KBYTES; };
     auto issue = [&](int st) {
         char* dst = (wv_v ? vslot(st) : kslot(st)) + wpage * C::LPS * 1024;
         const int kp = k_begin + st * C::SK + wpage * kPage;    // first key of this wave's page
@@ -270,57 +291,50 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         }
     };
 
-    // Per-lane V transpose-read addresses inside a V slot: the 16-lane groups
-    // read rows key0 = hl*4 + (lane&15)/4 (+ tile/k-step rows, immediates)
-    // at d = dt*32 + 16*((lane>>4)&1) + 4*(lane&3); the swizzle depends on
-    // key & 3 only, which the immediates do not change.
-    const int vkey = hl * 4 + ((lane & 15) >> 2);
-    int vcol[C::NDT];
-#pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) {
-        const int d = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-        vcol[dt] = vkey * ROWB + swz_v(vkey, d / 8, C::RC) * 16 + (d % 8) * 2;
-    }
-    // P^T fragments of the current tile (bf16, two 16-key k-steps)
-    bf16x8 pprev[2];
-    auto pv = [&](int tt, int st) {
-        const uint32_t vb = lds_u32(vslot(st));
-        uint32_t va[C::NDT];
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) va[dt] = vb + vcol[dt];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            s16x4 lo[C::NDT], hi[C::NDT];
-            if constexpr (C::NDT == 4) {
-                if (tt == 0 && kk == 0) tr_reads4<0, ROWB>(va, lo, hi);
-                else if (tt == 0) tr_reads4<16 * ROWB, ROWB>(va, lo, hi);
-                else if (kk == 0) tr_reads4<32 * ROWB, ROWB>(va, lo, hi);
-                else tr_reads4<48 * ROWB, ROWB>(va, lo, hi);
-            } else {
-                if (tt == 0 && kk == 0) tr_reads2<0, ROWB>(va, lo, hi);
-                else if (tt == 0) tr_reads2<16 * ROWB, ROWB>(va, lo, hi);
-                else if (kk == 0) tr_reads2<32 * ROWB, ROWB>(va, lo, hi);
-                else tr_reads2<48 * ROWB, ROWB>(va, lo, hi);
-            }
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) {
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pprev[kk], oacc[dt], 0, 0, 0);
-            }
-        }
-    };
-
-    // Software pipeline.  A wave owns one 32-key tile (tt_w) of every PER-th
-    // stage.  S^T of the tile of stage st is computed in iteration st; its
-    // softmax turns S into P (bf16) and its PV waits for iteration st+1, so
-    // V of stage st-1 must still be resident in iteration st: DMA runs
-    // NST-2 stages ahead (slot (st-2) % NST is refilled once every wave is
-    // past iteration st-1).
+    // A wave owns one 32-key tile (tt_w) of every PER-th stage.  S^T of the
+    // tile of stage st is computed in iteration st together with its
+    // softmax; its PV trails by one iteration, so V of stage st-1 must still
+    // be resident in iteration st (the V ring has one slot more than the K
+    // ring).
     constexpr int PER = NKG / 2;           // stages between two tiles of one wave (1, 2, 4)
     const int tt_w = kg % 2;               // this wave's tile inside its stages
     const int ph = kg / 2;                 // ... and which stages: st % PER == ph
 
-    // S^T = K Q^T for this wave's tile of stage st
+    // Per-lane V transpose-read addresses inside a V slot: the 16-lane groups
+    // read rows key0 = hl*4 + (lane&15)/4 (+ k-step rows, immediates) at
+    // d = dt*32 + 16*((lane>>4)&1) + 4*(lane&3); the swizzle depends on
+    // key & 3 only, which the immediates and the tile offset do not change.
+    const int vkey = hl * 4 + ((lane & 15) >> 2);
+    uint32_t vcol[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) {
+        const int d = dt * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
+        vcol[dt] = (uint32_t)(tt_w * 32 * ROWB + vkey * ROWB + swz_v(vkey, d / 8, C::RC) * 16 + (d % 8) * 2);
+    }
+
+    // V^T fragments of this wave's tile of stage st, both k-steps
+    s16x4 vt[4 * C::NDT];
+    auto pv_load = [&](int st) {
+        const uint32_t vb = lds_u32(vslot(st));
+        uint32_t va[C::NDT];
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) va[dt] = vb + vcol[dt];
+        if constexpr (C::NDT == 4) tr_tile4<ROWB>(va, vt);
+        else tr_tile2<ROWB>(va, vt);
+    };
+    // O^T += V^T P^T with the loaded fragments and the P of that tile
+    auto pv_mfma = [&](const bf16x8 (&p)[2]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                const s16x4 lo = vt[kk * 2 * C::NDT + dt], hi = vt[kk * 2 * C::NDT + C::NDT + dt];
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[kk], oacc[dt], 0, 0, 0);
+            }
+    };
+
+    // S^T = K Q^T for this wave's tile of stage st, causal mask applied
     auto qk = [&](int st, f32x16& sacc) {
         const int key = tt_w * 32 + col;
         const char* krow = kslot(st) + key * ROWB;
@@ -331,13 +345,6 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
-    };
-    // Online softmax of the tile of stage st in the log2 domain, with a
-    // lazily moved reference: m_run only moves when a row's tile maximum
-    // exceeds it by more than kLazy (then P <= 2^kLazy stays exact enough in
-    // bf16 and the fp32 sums), so the O rescale is rare.  O must already hold
-    // every PV before this tile's.
-    auto softmax = [&](int st, f32x16& sacc) {
         const int tb = k_begin + st * C::SK + tt_w * 32;   // first key of the tile
         if (tb + 31 > L) {        // uniform: only tiles reaching past the cached prefix
             asm volatile("");     // keep this a branch (no speculation into every tile)
@@ -346,56 +353,97 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
             for (int e = 0; e < 16; ++e)
                 if ((e >> 2) * 8 + (e & 3) > thr) sacc[e] = -INFINITY;
         }
+    };
+
+    // Online softmax in the log2 domain with a lazily moved reference: m_run
+    // only moves when a row's tile maximum exceeds it by more than kLazy
+    // (then P <= 2^kLazy stays exact enough in bf16 and the fp32 sums), so
+    // the O rescale is rare.  sm_core is branch-free (it is interleaved
+    // with MFMAs); sm_finish rescales O, which must already hold every PV
+    // before this tile's.  The row sum adds the bf16-rounded P that the PV
+    // contraction uses (dot2 with ones).
+    auto sm_core = [&](const f32x16& sacc, bf16x8 (&pn)[2], float& lsum, float& m_new, bool& need) {
         float mx = sacc[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
         mx = fmaxf(mx, other_half(mx, hl)) * a.scale_log2;
-        if (__any(mx > m_run + kLazy)) {
-            const float m_new = mx > m_run + kLazy ? mx : m_run;
+        need = mx > m_run + kLazy;
+        m_new = need ? mx : m_run;
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kk * 8 + e], a.scale_log2, -m_use));
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        lsum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 0, 1), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 2, 3), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 4, 5), ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 6, 7), ones, lsum, false);
+        }
+    };
+    auto sm_finish = [&](float lsum, float m_new, bool need) {
+        if (__any(need)) {
             const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < C::NDT; ++i)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-            m_run = m_new;
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kk * 8 + e], a.scale_log2, -m_use));
-                lsum += p;
-                pprev[kk][e] = (__bf16)p;
-            }
         l_run += lsum;
+        m_run = m_new;
     };
 
     // Ring step of stage st: this wave's loads of stage st landed (issued
-    // stages end at min(st+NST-3, n_stages-1)); the barrier makes every
-    // wave's part visible and frees slot (st-2) % NST for the next DMA.
+    // stages end at min(st+AHEAD-1, n_stages-1)); the barrier makes every
+    // wave's part visible and frees K slot (st-1) and V slot (st-2), whose
+    // last readers ran in iteration st-1, for the DMA of stage st+AHEAD.
     auto ring_step = [&](int st) {
-        if (st < n_stages) wait_stage<C::LPS, C::NST - 3>(min(C::NST - 3, n_stages - 1 - st));
+        if (st < n_stages) wait_stage<C::LPS, C::AHEAD - 1>(min(C::AHEAD - 1, n_stages - 1 - st));
         block_sync();
-        if (st + C::NST - 2 < n_stages) issue(st + C::NST - 2);
+        if (st + C::AHEAD < n_stages) issue(st + C::AHEAD);
     };
-    const int npro = n_stages < C::NST - 2 ? n_stages : C::NST - 2;
+    const int npro = n_stages < C::AHEAD ? n_stages : C::AHEAD;
     for (int st = 0; st < npro; ++st) issue(st);
     f32x16 sacc;
+    bf16x8 pprev[2];
     if constexpr (PER == 1) {
-        // The two waves of a SIMD (key groups 0 and 1 of one row group) work
-        // in opposite phase after each barrier: key group 0 runs its MFMAs
-        // (QK of st, PV of st-1) and then the softmax of st; key group 1 first
-        // runs the softmax of st-1 (S kept from the previous iteration), then
-        // the same MFMAs.  One wave's VALU work overlaps the other's MFMAs.
-        for (int st = 0; st <= n_stages; ++st) {
+        // Every wave has a tile in every stage.  Iteration st: QK of st; then
+        // the 2*NDT PV MFMAs of st-1 interleaved with the softmax VALU work
+        // of st in one straight-line region, so each MFMA's pipe time covers
+        // a share of the softmax.
+        for (int st = 0; st < n_stages; ++st) {
             ring_step(st);
-            if (kg == 1 && st >= 1) softmax(st - 1, sacc);
-            if (st < n_stages) qk(st, sacc);
-            if (st >= 1) pv(tt_w, st - 1);
-            if (kg == 0 && st < n_stages) softmax(st, sacc);
+            qk(st, sacc);
+            bf16x8 pn[2];
+            float lsum, m_new;
+            bool need;
+            if (st > 0) {
+                pv_load(st - 1);
+                pv_mfma(pprev);
+                sm_core(sacc, pn, lsum, m_new, need);
+#pragma unroll
+                for (int i = 0; i < 2 * C::NDT; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 32 / C::NDT, 0);    // then VALU
+                }
+                // keep P and its sum inside this region (the compiler would
+                // otherwise sink them below the rescale branch)
+                asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(lsum));
+            } else {
+                sm_core(sacc, pn, lsum, m_new, need);
+            }
+            sm_finish(lsum, m_new, need);
+            pprev[0] = pn[0];
+            pprev[1] = pn[1];
+        }
+        if (n_stages > 0) {
+            pv_load(n_stages - 1);
+            pv_mfma(pprev);
         }
     } else {
         for (int st = 0; st <= n_stages; ++st) {
@@ -403,8 +451,19 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
             const bool cur = st < n_stages && (st % PER) == ph;
             const bool prev = st >= 1 && ((st - 1) % PER) == ph;
             if (cur) qk(st, sacc);
-            if (prev) pv(tt_w, st - 1);
-            if (cur) softmax(st, sacc);
+            if (prev) {
+                pv_load(st - 1);
+                pv_mfma(pprev);
+            }
+            if (cur) {
+                bf16x8 pn[2];
+                float lsum, m_new;
+                bool need;
+                sm_core(sacc, pn, lsum, m_new, need);
+                sm_finish(lsum, m_new, need);
+                pprev[0] = pn[0];
+                pprev[1] = pn[1];
+            }
         }
     }
 
