@@ -192,6 +192,7 @@ extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const v
     a.B = s->B; a.W = s->W; a.Hq = s->Hq; a.Hkv = s->Hkv; a.G = s->Hq / s->Hkv; a.M = s->W * a.G;
     a.max_pages = s->max_pages; a.num_pages = s->num_pages;
     a.RT = p.RT; a.row_tiles = p.row_tiles; a.nsplit = p.nsplit; a.split_keys = p.split_keys;
+    a.split_align = p.chunk;
     a.max_ctx = max_ctx_len;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)s->D);
     a.scale_log2 = sc * kLog2e;

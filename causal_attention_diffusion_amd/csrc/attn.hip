@@ -103,8 +103,9 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
         L = 0;
     }
     const int T_len = ctx_ok ? L + a.W : 0;
-    const int k_begin = split * a.split_keys;
-    const int k_end = min(T_len, k_begin + a.split_keys);
+    const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
+    const int k_begin = split * sk;
+    const int k_end = min(T_len, k_begin + sk);
     if (k_begin >= k_end && a.nsplit > 1) return;  // merged away by attn_combine
 
     // block-table slice of this split
@@ -367,7 +368,8 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     const int L = a.ctx_len[b];
     const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
     const int T_len = ctx_ok ? L + a.W : 0;
-    const int nvalid = min(a.nsplit, (T_len + a.split_keys - 1) / a.split_keys);
+    const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
+    const int nvalid = min(a.nsplit, (T_len + sk - 1) / sk);
     const size_t base = (size_t)pid * a.nsplit * a.RT + m_loc;
     const float* po = a.part_o + base * D + d;
     const size_t stride = (size_t)a.RT * D;

@@ -50,7 +50,8 @@ struct Bf16Cfg {
     static_assert(LPS * 1024 * NWAVES == STAGE, "stage must split into whole wave loads");
 };
 
-constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised P
+constexpr float kLazy = 8.0f;    // log2 of the largest unnormalised P
+constexpr float kLazyP = 256.0f; // 2^kLazy
 // cache policy of the K/V loads: non-temporal (every byte is read once per
 // launch; measured 7 % faster streaming than the default policy)
 constexpr int kNT = 2;
@@ -189,8 +190,9 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         L = 0;
     }
     const int T_len = ctx_ok ? L + a.W : 0;
-    const int k_begin = split * a.split_keys;
-    const int k_end = min(T_len, k_begin + a.split_keys);
+    const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
+    const int k_begin = split * sk;
+    const int k_end = min(T_len, k_begin + sk);
     if (k_begin >= k_end && a.nsplit > 1) return;  // nothing here; attn_combine skips this split
 
     const int p0 = k_begin / kPage;
@@ -217,7 +219,11 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
             const uint4 v = row_ok ? qp[s * 2 + hl] : make_uint4(0, 0, 0, 0);
-            qf[s] = __builtin_bit_cast(bf16x8, v);
+            // Q scaled by softmax scale * log2(e) and rounded to bf16 once, so
+            // S comes out of the MFMA in log2 units
+            const bf16x8 raw = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)raw[e] * a.scale_log2);
         }
     }
     f32x16 oacc[C::NDT];
@@ -225,7 +231,15 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     for (int i = 0; i < C::NDT; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    // Softmax state of this lane's row: the reference m_ref (log2 units),
+    // applied through the QK accumulator's initial value -m_ref (negm, one
+    // copy per accumulator element), whether the row has seen a visible key
+    // yet, and the running sum l_run.
+    float m_ref = 0.f, l_run = 0.f;
+    bool started = false;
+    f32x16 negm;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) negm[e] = 0.f;
 
     __syncthreads();  // s_pages visible; Q loads may still be in flight (waited below)
     wait_vm<0>();     // the Q loads count in vmcnt: retire them before the ring accounting starts
@@ -341,10 +355,9 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         bf16x8 kf[D / 16];
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + swz_k(key, 2 * s + hl, C::RC) * 16);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], negm, 0, 0, 0);   // starts at -m_ref
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+        for (int s = 1; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
         const int tb = k_begin + st * C::SK + tt_w * 32;   // first key of the tile
         if (tb + 31 > L) {        // uniform: only tiles reaching past the cached prefix
             asm volatile("");     // keep this a branch (no speculation into every tile)
@@ -355,47 +368,65 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         }
     };
 
-    // Online softmax in the log2 domain with a lazily moved reference: m_run
-    // only moves when a row's tile maximum exceeds it by more than kLazy
-    // (then P <= 2^kLazy stays exact enough in bf16 and the fp32 sums), so
-    // the O rescale is rare.  sm_core is branch-free (it is interleaved
-    // with MFMAs); sm_finish rescales O, which must already hold every PV
-    // before this tile's.  The row sum adds the bf16-rounded P that the PV
-    // contraction uses (dot2 with ones).
-    auto sm_core = [&](const f32x16& sacc, bf16x8 (&pn)[2], float& lsum, float& m_new, bool& need) {
-        float mx = sacc[0];
+    // Online softmax in the log2 domain with a lazily moved reference.  The
+    // accumulator already holds S - m_ref, so P = 2^(S - m_ref) is one
+    // v_exp per score (sm_core, branch-free: it is interleaved with MFMAs).
+    // The reference only has to keep P in range: sm_finish moves it when a
+    // row has not seen a visible key yet or when this lane's 16 P sum past
+    // 2^kLazy (so every P <= 2^kLazy holds, as with a max test; inf and NaN
+    // sums also fail the test).  Then it takes the true tile maximum, moves
+    // m_ref up to it when it exceeds m_ref by more than kLazy, rescales O and
+    // l (O must already hold every PV before this tile's) and recomputes P.
+    // The row sum adds the bf16-rounded P that the PV contraction uses.
+    auto p_sum = [&](const bf16x8 (&pn)[2]) {
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float ls = 0.f;
 #pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-        mx = fmaxf(mx, other_half(mx, hl)) * a.scale_log2;
-        need = mx > m_run + kLazy;
-        m_new = need ? mx : m_run;
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        for (int kk = 0; kk < 2; ++kk) {
+            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 0, 1), ones, ls, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 2, 3), ones, ls, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 4, 5), ones, ls, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 6, 7), ones, ls, false);
+        }
+        return ls;
+    };
+    auto sm_core = [&](const f32x16& sacc, bf16x8 (&pn)[2], float& lsum, bool& need) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kk * 8 + e], a.scale_log2, -m_use));
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        lsum = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 0, 1), ones, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 2, 3), ones, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 4, 5), ones, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pn[kk], pn[kk], 6, 7), ones, lsum, false);
-        }
+            for (int e = 0; e < 8; ++e) pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kk * 8 + e]);
+        lsum = p_sum(pn);
+        need = !started || !(lsum <= kLazyP);
     };
-    auto sm_finish = [&](float lsum, float m_new, bool need) {
+    auto sm_finish = [&](const f32x16& sacc, bf16x8 (&pn)[2], float& lsum, bool need) {
         if (__any(need)) {
-            const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
+            float mx = sacc[0];
 #pragma unroll
-            for (int i = 0; i < C::NDT; ++i)
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+            mx = fmaxf(mx, other_half(mx, hl)) + m_ref;              // true tile maximum
+            const bool vis = mx != -INFINITY;
+            const float m_new = started ? (mx > m_ref + kLazy ? mx : m_ref) : (vis ? mx : m_ref);
+            if (__any(m_new != m_ref)) {
+                // rows that had not started hold O = 0 and l = 0
+                const float alpha = (started && m_new != m_ref) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+                l_run *= alpha;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+                for (int i = 0; i < C::NDT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+            }
+            const float sh = m_ref - m_new;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kk * 8 + e] + sh);
+            lsum = p_sum(pn);
+            m_ref = m_new;
+            started = started || vis;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) negm[e] = -m_ref;
         }
         l_run += lsum;
-        m_run = m_new;
     };
 
     // Ring step of stage st: this wave's loads of stage st landed (issued
@@ -420,12 +451,12 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
             ring_step(st);
             qk(st, sacc);
             bf16x8 pn[2];
-            float lsum, m_new;
+            float lsum;
             bool need;
             if (st > 0) {
                 pv_load(st - 1);
                 pv_mfma(pprev);
-                sm_core(sacc, pn, lsum, m_new, need);
+                sm_core(sacc, pn, lsum, need);
 #pragma unroll
                 for (int i = 0; i < 2 * C::NDT; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
@@ -435,9 +466,9 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
                 // otherwise sink them below the rescale branch)
                 asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(lsum));
             } else {
-                sm_core(sacc, pn, lsum, m_new, need);
+                sm_core(sacc, pn, lsum, need);
             }
-            sm_finish(lsum, m_new, need);
+            sm_finish(sacc, pn, lsum, need);
             pprev[0] = pn[0];
             pprev[1] = pn[1];
         }
@@ -457,10 +488,10 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
             }
             if (cur) {
                 bf16x8 pn[2];
-                float lsum, m_new;
+                float lsum;
                 bool need;
-                sm_core(sacc, pn, lsum, m_new, need);
-                sm_finish(lsum, m_new, need);
+                sm_core(sacc, pn, lsum, need);
+                sm_finish(sacc, pn, lsum, need);
                 pprev[0] = pn[0];
                 pprev[1] = pn[1];
             }
@@ -482,7 +513,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
             for (int g4 = 0; g4 < 4; ++g4)
                 *reinterpret_cast<float4*>(dst + dt * 32 + hl * 4 + g4 * 8) =
                     make_float4(oacc[dt][g4 * 4 + 0], oacc[dt][g4 * 4 + 1], oacc[dt][g4 * 4 + 2], oacc[dt][g4 * 4 + 3]);
-        if (hl == 0) s_ml[kg][row] = make_float2(m_run, l_tot);
+        if (hl == 0) s_ml[kg][row] = make_float2(started ? m_ref : -INFINITY, l_tot);
     }
     __syncthreads();
 

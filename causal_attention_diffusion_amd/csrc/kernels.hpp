@@ -37,7 +37,8 @@ struct AttnArgs {
     float2* part_ml; // [npid][nsplit][RT]  (m in log2 units, l)
     int32_t* status;
     int B, W, Hq, Hkv, G, M, max_pages, num_pages;
-    int RT, row_tiles, nsplit, split_keys;
+    int RT, row_tiles, nsplit, split_keys;  // split_keys: largest split (host bound)
+    int split_align;   // keys per ring stage of the split kernel (64 bf16, 32 fp32)
     int max_ctx;       // host bound on ctx_len: the split grid covers max_ctx + W keys
     float scale_log2;  // softmax scale * log2(e)
 };
@@ -57,6 +58,18 @@ struct SelectArgs {
     float alpha, tau;
     int mask_id;
 };
+
+// Keys per split of one sequence: its visible keys T_len spread evenly over
+// the grid's nsplit work-groups, rounded up to the ring stage `align` and
+// never above split_keys (the host sized split_keys * nsplit for the longest
+// admissible context, so the bound only bites there).  The split kernels and
+// the combine use this same rule.
+__device__ __forceinline__ int split_len(int T_len, int nsplit, int split_keys, int align) {
+    int sk = (T_len + nsplit - 1) / nsplit;
+    sk = (sk + align - 1) / align * align;
+    if (sk < align) sk = align;
+    return sk < split_keys ? sk : split_keys;
+}
 
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
