@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = auto)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each attention call after a 1 GiB scratch write (MALL cold)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -161,6 +163,23 @@ def main():
     attn_avg_ms = ev0.elapsed_time(ev1) / args.steps
     L_now = ctx.cpu().numpy().astype(np.int64)
 
+    # optional: the same call with the 256 MB MALL flushed before each launch
+    # (a 1 GiB scratch write), timed launch by launch
+    attn_cold_ms = None
+    if args.cold:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        tot = 0.0
+        for _ in range(args.steps):
+            scratch.fill_(1.0)
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            attention()
+            eb.record(stream)
+            eb.synchronize()
+            tot += ea.elapsed_time(eb)
+        attn_cold_ms = tot / args.steps
+        del scratch
+
     # ---- timed region 3: the select/commit call alone on the last logits
     # buffer (state restored after), for its own bandwidth figure
     saved = [x.clone() for x in (tok, filled, pos, ctx)]
@@ -195,6 +214,10 @@ def main():
     # of every visible key read once, Q read, O written
     mean_attn_bytes = float(((L_now + W) * Hkv * D * 2 * eb).sum() + 2 * B * W * Hq * D * eb)
     achieved = mean_attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    # algorithmic flops: row r of a window sees L_b + r + 1 keys; 2D for QK
+    # and 2D for PV per (row, key, query head)
+    attn_flops = float((4 * D * Hq * (W * L_now + W * (W + 1) // 2)).sum())
+    mfma_peak = 2.5e15 if cfg.dtype == "bf16" else 157.3e12
     tokens_per_s = B * W / (ms_step * 1e-3)
     masked_rows = (argmax_hist[args.warmup:] >= 0).sum(dim=(1, 2)).cpu().numpy()
     sel_bytes = nmask * args.vocab * 4                                     # logits rows actually read
@@ -220,10 +243,18 @@ def main():
                    "vocab": args.vocab, "split_kv": [nsplit, split_keys]},
         "steps_per_s": round(1e3 / ms_step, 2),
         "attn": {"avg_ms": round(attn_avg_ms, 5), "alg_bytes_per_launch": int(mean_attn_bytes),
-                 "GB_per_s": round(achieved, 1), "prefix_tokens": [int(x) for x in L_now]},
+                 "GB_per_s": round(achieved, 1), "prefix_tokens": [int(x) for x in L_now],
+                 "alg_flops_per_launch": int(attn_flops),
+                 "TFLOP_per_s": round(attn_flops / (attn_avg_ms * 1e-3) / 1e12, 1),
+                 "mfma_frac_of_dense_peak": round(attn_flops / (attn_avg_ms * 1e-3) / mfma_peak, 4),
+                 **({"cold_avg_ms": round(attn_cold_ms, 5),
+                     "cold_GB_per_s": round(mean_attn_bytes / (attn_cold_ms * 1e-3) / 1e9, 1)}
+                    if attn_cold_ms is not None else {})},
         "select_commit": {"avg_ms": round(sel_ms, 5), "masked_rows": nmask, "GB_per_s": round(sel_gbs, 1),
                           "masked_rows_per_step_in_stream": float(masked_rows.mean())},
         "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
+        # P_c: committed tokens over window slots processed, over the timed steps
+        "P_c": round(float(nc.sum()) / (K * B * W), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args),
                      "kernel": "wedlm_step_attn (attn_split + attn_combine)"},

@@ -106,6 +106,23 @@ def test_reorder_parity(name, dev):
     assert torch.equal(t["v_cache"].permute(0, 2, 1, 3)[keep], vc0.permute(0, 2, 1, 3)[keep])
 
 
+def test_reorder_retry_is_idempotent(dev):
+    """A repeated wedlm_reorder on the same window state rewrites only the
+    window's cache rows [L, L+W) with the same bytes: a retried step is safe."""
+    cfg = wl.CONFIGS["ragged_b32"]
+    print("[reorder retry] ragged_b32", flush=True)
+    inp = wl.make_attn_inputs(cfg)
+    t = wl.device_attn_inputs(inp, dev)
+    run_reorder(t, cfg)
+    torch.cuda.synchronize()
+    first = {k: t[k].clone() for k in ("q_phys", "k_cache", "v_cache", "perm")}
+    run_reorder(t, cfg)
+    torch.cuda.synchronize()
+    assert t["status"].item() == 0
+    for k, v in first.items():
+        assert torch.equal(t[k], v), k
+
+
 # ---------------------------------------------------------------- attention alone
 def _attn_alone(cfg, dev, n_rows=None, seed=None):
     inp, q_phys, dk, dv = wl.make_full_cache_inputs(cfg, seed)
