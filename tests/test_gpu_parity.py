@@ -157,6 +157,19 @@ def test_attention_parity(name, n_rows, dev):
     assert err <= ATTN_TOL[cfg.dtype], err
 
 
+def test_attention_at_maximum_context(dev):
+    """The longest context the call accepts: 524288 keys including the
+    window, planned as 64 splits of 8192 keys (the combine's limit and the
+    largest block-table slice), on one KV head; sampled rows vs the oracle."""
+    cfg = _cfg("qwen3_l2048", name="max_ctx", B=1, W=16, L=524288 - 16, n_obs=5, Hq=4, Hkv=1,
+               dtype="bf16")
+    print("[attn] max context 524288", flush=True)
+    err, status = _attn_alone(cfg, dev, n_rows=24)
+    print(f"[attn] max context: max|gpu-oracle|/max|oracle| = {err:.3e}")
+    assert status == 0
+    assert err <= ATTN_TOL["bf16"], err
+
+
 # ---------------------------------------------------------------- reorder + attention
 @pytest.mark.parametrize("name,n_rows", [("tiny_f32", None), ("qwen3_l2048", None),
                                          ("ragged_b32", 256), ("long_b4", 128)])
@@ -186,6 +199,7 @@ EDGE = [
     ("W64_G4", dict(B=1, W=64, L=300, n_obs=20, dtype="bf16"), 0),
     ("G1_D64", dict(B=2, W=16, L=77, n_obs=5, Hq=8, Hkv=8, D=64, dtype="bf16"), 0),
     ("G8", dict(B=2, W=16, L=129, n_obs=7, Hq=32, Hkv=4, dtype="bf16"), 0),
+    ("W64_G8_rowtiles4", dict(B=1, W=64, L=200, n_obs=31, Hq=64, Hkv=8, dtype="bf16"), 0),
     ("ragged_tails_split64", dict(B=6, W=16, L_range=(1, 200), n_obs=None, dtype="bf16"), 64),
     ("ragged_tails_split128", dict(B=6, W=16, L_range=(1, 200), n_obs=None, dtype="bf16"), 128),
     ("f32_D128_split64", dict(B=2, W=8, L=150, n_obs=3, Hq=8, Hkv=2, D=128, dtype="f32",
