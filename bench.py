@@ -16,7 +16,10 @@ tokens in 16-token pages (shuffled), window 32 (16 observed), bf16; logits
 
 Prints one JSON line (rank 0).  Three timed regions: (1) K whole streaming
 steps, bracketed by device synchronisation, give ms_per_step and the
-headline window tokens/s; (2) K back-to-back launches of the attention call
+headline window tokens/s: launched eagerly (reported as eager_ms_per_step),
+then, unless --eager, the same K steps captured once as a HIP graph and
+replayed from the same starting state, as a serving loop would run them
+(this replay gives ms_per_step and the value); (2) K back-to-back launches of the attention call
 on the final state, bracketed by HIP events on its stream, give the mean
 launch time the roofline divides the launch's algorithmic bytes (K/V of
 every visible key read once, Q in, O out) by; (3) the select/commit call
@@ -55,6 +58,9 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = auto)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time only eager launches (default: eager, then the same K steps replayed "
+                         "as one captured HIP graph, which gives the reported value)")
     ap.add_argument("--cold", action="store_true",
                     help="also time each attention call after a 1 GiB scratch write (MALL cold)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -141,13 +147,38 @@ def main():
     torch.cuda.synchronize()
     ctx_start = ctx.cpu().numpy().astype(np.int64)
 
-    # ---- timed region 1: K whole streaming steps, nothing else on the stream
+    # ---- timed region 1: K whole streaming steps, nothing else on the stream.
+    # First launched eagerly; then (default) the same K steps captured once
+    # into a HIP graph and replayed from the same post-warm-up state, once
+    # untimed and once timed.  Capture records without running; a replay from
+    # the same state rewrites the same cache rows with the same bytes.
+    state0 = [x.clone() for x in (tok, filled, pos, ctx)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, total_steps):
         step(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    eager_elapsed = time.perf_counter() - t0
+    elapsed = eager_elapsed
+    if not args.eager:
+        for x, y in zip((tok, filled, pos, ctx), state0):
+            x.copy_(y)
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.warmup, total_steps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(2):
+            for x, y in zip((tok, filled, pos, ctx), state0):
+                x.copy_(y)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
 
     # ---- timed region 2: the attention call alone, K launches back to back on
     # the stream it runs on (the state the stream ended in), bracketed by HIP
@@ -236,6 +267,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "graph": not args.eager,
+        "eager_ms_per_step": round(eager_elapsed * 1e3 / args.steps, 4),
         "config": {"workload": f"{cfg.name}: B={B} W={W} Hq={Hq} Hkv={Hkv} D={D} "
                                f"prefix={int(inp.ctx_len.max()) if cfg.L_range is None else str(cfg.L_range)} "
                                f"page=16 vocab={args.vocab} streaming decode step (reorder+attn+select/commit)",
