@@ -90,7 +90,7 @@ static int device_cus() {
     }
     return cache[dev];
 }
-static const int64_t kMaxContext = 64ll * kMaxSplitPages * kPage;  // 524288 keys incl. the window
+static const int64_t kMaxContext = 524288;  // keys incl. the window (at most 64 splits of 8192)
 
 struct Plan {
     int nw, chunk, RT, row_tiles, nsplit, split_keys;

@@ -6,7 +6,7 @@
 
 namespace wedlm {
 
-constexpr int kMaxSplitPages = 512;  // LDS block-table slice of a split: split_keys <= 8192
+constexpr int kMaxSplitPages = 2048;  // LDS block-table slice of a split: split_keys <= 32768
 
 struct ReorderArgs {
     const uint8_t* filled;

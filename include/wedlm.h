@@ -212,7 +212,7 @@ int wedlm_attn_plan(const wedlm_shape *s, int32_t max_ctx_len, int32_t *nsplit,
 
 /*
  * wedlm_set_attn_split_keys -- process-wide override of the keys per
- * split-KV work-group (a multiple of 64, 64..8192), 0 restores the
+ * split-KV work-group (a multiple of 64, 64..32768), 0 restores the
  * automatic choice.  Affects later workspace queries and calls alike.
  */
 int wedlm_set_attn_split_keys(int32_t keys);

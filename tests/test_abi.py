@@ -111,7 +111,7 @@ def test_step_attn_validation():
 def test_attention_plan_covers_every_key(B, W, Hq, Hkv, D, dt, L):
     mp = (L + W + 15) // 16
     ns, sk = wd.attn_plan(B, W, Hq, Hkv, D, mp, B * mp, dt, L)
-    assert ns >= 1 and sk >= 32 and sk % 32 == 0 and sk <= 8192
+    assert ns >= 1 and sk >= 32 and sk % 32 == 0 and sk <= 32768
     assert ns * sk >= L + W                 # the grid covers every visible key
     assert (ns - 1) * sk < L + W            # and no split is wholly past the end
     s = _shape(B=B, W=W, Hq=Hq, Hkv=Hkv, D=D, max_pages=mp, num_pages=B * mp, dtype=dt)
