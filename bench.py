@@ -52,7 +52,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_b4",
-                    choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32"])
+                    choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32", "select_v152k"],
+                    help="select_v152k times the select/commit call alone (batch 64 x window 16, "
+                         "V=151936, streaming from an all-masked window)")
     ap.add_argument("--vocab", type=int, default=151936)
     ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
@@ -94,6 +96,10 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(see the sharding paragraph of DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "select_v152k":
+        bench_select(args)
+        return
 
     import torch
     import workloads as wl
@@ -296,6 +302,130 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, args, inp)
     print(json.dumps(result), flush=True)
+
+
+def bench_select(args):
+    """The select/commit call alone, streaming: batch 64 x window 16 over
+    V=151936 fp32 logits, starting from an all-masked window at prefix 0.  A
+    step is one wedlm_select_commit (vocabulary statistics of every masked
+    slot, commit, Eq. 11 fill, refill); the logits of step i are buffer
+    i mod --logit-ring (each 622 MB, so none stays in the 256 MB MALL)."""
+    import torch
+    import workloads as wl
+    import causal_attention_diffusion_amd as wd
+
+    dev = torch.device("cuda:0")
+    cfg = wl.SELECT_CONFIGS["select_v152k"]
+    B, W, V = cfg.B, cfg.W, cfg.V
+    total = args.warmup + args.steps
+    logits = [wl.make_logits_torch(cfg, i, dev) for i in range(args.logit_ring)]
+    ws = wd.select_workspace_tensor(B, W, V, dev)
+    init = [torch.from_numpy(x).to(dev) for x in wl.initial_window(B, W, V)]
+    tok, filled, pos, ctx = [x.clone() for x in init]
+    n_commit_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    committed = torch.empty((B, W), dtype=torch.int32, device=dev)
+    argmax_hist = torch.empty((total, B, W), dtype=torch.int32, device=dev)  # -1 on unmasked slots
+
+    def step(i):
+        wd.wedlm_select_commit(logits[i % len(logits)], tok, filled, pos, ctx, n_commit_hist[i], committed,
+                               cfg.alpha, cfg.tau, V, ws, argmax_out=argmax_hist[i])
+
+    def reset():
+        for x, y in zip((tok, filled, pos, ctx), init):
+            x.copy_(y)
+
+    for i in range(args.warmup):
+        step(i)
+    # timed: K steps from the all-masked start, eagerly (HIP events on the
+    # stream bracket exactly the K calls), then replayed as one HIP graph
+    reset()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.warmup, total):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    eager_elapsed = time.perf_counter() - t0
+    call_ms = ev0.elapsed_time(ev1) / args.steps
+    state_eager = [x.clone() for x in (tok, filled, pos, ctx)]
+    elapsed = eager_elapsed
+    if not args.eager:
+        reset()
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.warmup, total):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(2):
+            reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+        for x, y in zip((tok, filled, pos, ctx), state_eager):
+            if not torch.equal(x, y):
+                print("graph replay diverged from the eager steps", file=sys.stderr)
+                sys.exit(3)
+
+    K = args.steps
+    ms_step = elapsed * 1e3 / K
+    masked = (argmax_hist[args.warmup:] >= 0).sum(dim=(1, 2)).cpu().numpy().astype(np.int64)
+    nc = n_commit_hist[args.warmup:].cpu().numpy().astype(np.int64)
+    # algorithmic bytes: every masked slot's logits row read once
+    alg_bytes = float(masked.sum()) * V * 4 / K
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(B * W / (ms_step * 1e-3), 1),
+        "unit": "window tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "graph": not args.eager,
+        "eager_ms_per_step": round(eager_elapsed * 1e3 / K, 4),
+        "config": {"workload": f"select_v152k: B={B} W={W} vocab={V} fp32 logits (low/high-entropy "
+                               f"mixture), alpha={cfg.alpha} tau={cfg.tau}, {K} streaming select/commit "
+                               f"steps from an all-masked window",
+                   "batch": B, "window": W, "vocab": V, "logit_buffers": len(logits)},
+        "steps_per_s": round(1e3 / ms_step, 2),
+        "select_commit": {"avg_ms": round(call_ms, 5), "alg_bytes_per_launch": int(alg_bytes),
+                          "masked_rows_per_step": round(float(masked.mean()), 2),
+                          "GB_per_s": round(achieved, 1)},
+        "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
+        "P_c": round(float(nc.sum()) / (K * B * W), 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "wedlm_select_commit (vocab_stats + commit_select_refill)"},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_select(cfg, args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_select(cfg, args):
+    """The oracle's select/commit step, untuned, on the host cores, over the
+    whole batch from the all-masked start (every row masked: the largest
+    step of the stream), in window tokens/s."""
+    import oracle
+    import workloads as wl
+    lg = wl.make_logits_np(cfg, 0)
+    tok, filled, pos, ctx = wl.initial_window(cfg.B, cfg.W, cfg.V)
+    reps, dt_s = 0, 0.0
+    while reps < 64 and dt_s < 10.0:
+        t0 = time.perf_counter()
+        oracle.select_commit(lg, tok, filled, pos, ctx, cfg.alpha, cfg.tau, cfg.V)
+        dt_s += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(reps * cfg.B * cfg.W / dt_s, 1), "unit": "window tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the first step ({cfg.B} x {cfg.W} masked rows over V={cfg.V}) repeated {reps}x; "
+                      f"{dt_s:.2f} s"}
 
 
 def attn_source_hash():

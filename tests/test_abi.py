@@ -123,7 +123,7 @@ def test_split_override_validation():
     with pytest.raises(wd.WedlmError):
         wd.wedlm_set_attn_split_keys(100)
     with pytest.raises(wd.WedlmError):
-        wd.wedlm_set_attn_split_keys(16384)
+        wd.wedlm_set_attn_split_keys(32768 + 64)
     wd.wedlm_set_attn_split_keys(128)
     try:
         ns, sk = wd.attn_plan(1, 16, 32, 8, 128, 200, 200, 1, 3000)
