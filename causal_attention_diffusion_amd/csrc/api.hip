@@ -200,11 +200,13 @@ extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const v
 }
 
 // ---------------------------------------------------------------- select / commit
-static const int kPartLen = 16384;  // logits per work-group: 256 threads x 16 float4
+static const int kPartLen = 16384;  // most logits per work-group: 256 threads x 16 float4
 
+// Parts of a row: as few as kPartLen allows, of equal length (a multiple of
+// 4) so that no work-group is left with a short tail.
 static void select_plan(int32_t V, int* nparts, int* part_len) {
-    int pl = kPartLen;
-    if (V < pl) pl = (V + 3) / 4 * 4;
+    const int np = (V + kPartLen - 1) / kPartLen;
+    const int pl = ((V + np - 1) / np + 3) / 4 * 4;
     *part_len = pl;
     *nparts = (V + pl - 1) / pl;
 }

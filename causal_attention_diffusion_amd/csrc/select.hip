@@ -66,40 +66,39 @@ __device__ __forceinline__ void raise_max(Stat& st, float bm, int ba) {
 // Add exp terms of one value (its maximum is already folded into st.m).
 __device__ __forceinline__ void add_term(float& s, float& t, float z, float m) {
     // (z - m) first: exact 0 at the maximum, so a row with one dominant
-    // logit gets exactly S = 1, T = 0 there (H = 0 for a certain row)
-    const float u = (z - m) * kLog2e;
+    // logit gets exactly S = 1, T = 0 there (H = 0 for a certain row).  The
+    // clamp at -200 (2^-200 is 0 in fp32) keeps u * 2^u = 0 for -inf
+    // logits and padding instead of -inf * 0.
+    const float u = fmaxf((z - m) * kLog2e, -200.f);
     const float e = __builtin_amdgcn_exp2f(u);
     s += e;
     t = fmaf(u, e, t);
 }
 
-// Fold K float4 (element j of v[k] has index base + 1024 k + j, increasing
-// in visiting order) into st: one max test per batch.
+// Fold K 4-vectors (element j of v[k] has index base + 1024 k + j,
+// increasing in visiting order) into st: one max test per batch.  Padding
+// entries hold -inf: they never become the maximum and add 0 to S and T.
 template <int K>
-__device__ __forceinline__ void accum_vec(Stat& st, const float4 (&v)[K], int base) {
-    float bm = fmaxf(fmaxf(v[0].x, v[0].y), fmaxf(v[0].z, v[0].w));
+__device__ __forceinline__ void accum_vec(Stat& st, const f32x4 (&v)[K], int base) {
+    float bm = fmaxf(fmaxf(v[0][0], v[0][1]), fmaxf(v[0][2], v[0][3]));
 #pragma unroll
-    for (int k = 1; k < K; ++k) bm = fmaxf(bm, fmaxf(fmaxf(v[k].x, v[k].y), fmaxf(v[k].z, v[k].w)));
+    for (int k = 1; k < K; ++k) bm = fmaxf(bm, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
     if (bm > st.m) {
         int ba = 0x7fffffff;
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {   // backwards, so the first match wins
             const int i0 = base + 1024 * k;
-            if (v[k].w == bm) ba = i0 + 3;
-            if (v[k].z == bm) ba = i0 + 2;
-            if (v[k].y == bm) ba = i0 + 1;
-            if (v[k].x == bm) ba = i0;
+#pragma unroll
+            for (int j = 3; j >= 0; --j)
+                if (v[k][j] == bm) ba = i0 + j;
         }
         raise_max(st, bm, ba);
     }
     float s = 0.f, t = 0.f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        add_term(s, t, v[k].x, st.m);
-        add_term(s, t, v[k].y, st.m);
-        add_term(s, t, v[k].z, st.m);
-        add_term(s, t, v[k].w, st.m);
-    }
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) add_term(s, t, v[k][j], st.m);
     st.s += s;
     st.t += t;
 }
@@ -139,22 +138,19 @@ __global__ __launch_bounds__(256) void vocab_stats(SelectArgs a) {
         const float* z = a.logits + (size_t)row * a.V;
         Stat st{-INFINITY, 0x7fffffff, 0.f, 0.f};
         if constexpr (VEC) {
-            // part_len and beg are multiples of 4 and V % 4 == 0; a full part
-            // is kVecPerThread float4 per thread, all loads issued up front
-            const float4* z4 = reinterpret_cast<const float4*>(z);
+            // part_len and beg are multiples of 4 and V % 4 == 0; a part is at
+            // most kVecPerThread 16-byte loads per thread, all issued up front
+            // (non-temporal: every logit is read once), -inf past its end
+            const f32x4* z4 = reinterpret_cast<const f32x4*>(z);
             const int n4 = (end - beg) / 4;
             const int b4 = beg / 4;
-            if (n4 == kVecPerThread * 256) {
-                float4 v[kVecPerThread];
+            f32x4 v[kVecPerThread];
 #pragma unroll
-                for (int k = 0; k < kVecPerThread; ++k) v[k] = z4[b4 + tid + k * 256];
-                accum_vec(st, v, (b4 + tid) * 4);
-            } else {
-                for (int i = tid; i < n4; i += 256) {
-                    const float4 v1[1] = {z4[b4 + i]};
-                    accum_vec(st, v1, (b4 + i) * 4);
-                }
+            for (int k = 0; k < kVecPerThread; ++k) {
+                const int i = tid + k * 256;
+                v[k] = i < n4 ? __builtin_nontemporal_load(z4 + b4 + i) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
             }
+            accum_vec(st, v, (b4 + tid) * 4);
         } else {
             for (int i = beg + tid; i < end; i += 256) accum_one(st, z[i], i);
         }
@@ -182,27 +178,32 @@ __global__ __launch_bounds__(64) void commit_select_refill(SelectArgs a) {
     const int j = lane;
     const bool in = j < W;
     const size_t sj = (size_t)b * W + j;
+    const int L = a.ctx_len[b];
     int tk = in ? a.tok[sj] : a.mask_id;
     int f = in ? a.filled[sj] : 1;
+    // The row partials are read for every slot in the window, 16 at a time
+    // with all loads in flight, so that they do not wait for the flags; only
+    // the masked slots' (written by vocab_stats) are used.
+    Stat o{-INFINITY, 0x7fffffff, 0.f, 0.f};
+    if (in) {
+        const float4* pp = a.part + sj * a.nparts;
+        for (int p0 = 0; p0 < a.nparts; p0 += 16) {
+            float4 v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = p0 + q < a.nparts ? pp[p0 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const Stat x{v[q].x, __float_as_int(v[q].y), v[q].z, v[q].w};  // s == 0: empty, skipped
+                o = merge(o, x);
+            }
+        }
+    }
     const uint64_t fmask = __ballot(in && f != 0);
     const int k = ~fmask ? (int)__builtin_ctzll(~fmask) : 64;  // leading run of filled slots (<= W)
     const bool msk = in && f == 0;
     float H = -1.f;
     int am = -1;
     if (msk) {
-        // partials are loaded 8 at a time so their latencies overlap
-        Stat o{-INFINITY, 0x7fffffff, 0.f, 0.f};
-        const float4* pp = a.part + sj * a.nparts;
-        for (int p0 = 0; p0 < a.nparts; p0 += 8) {
-            float4 v[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = p0 + q < a.nparts ? pp[p0 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const Stat x{v[q].x, __float_as_int(v[q].y), v[q].z, v[q].w};  // s == 0: empty, skipped
-                o = merge(o, x);
-            }
-        }
         am = o.a;
         H = logf(o.s) - 0.69314718055994531f * (o.t / o.s);
     }
@@ -235,7 +236,6 @@ __global__ __launch_bounds__(64) void commit_select_refill(SelectArgs a) {
     const int src = j + k;
     const int tk_s = __shfl(tk, src < 64 ? src : 0);
     const int f_s = __shfl(f, src < 64 ? src : 0);
-    const int L = a.ctx_len[b];
     if (in) {
         const bool keep = src < W;
         a.tok[sj] = keep ? tk_s : a.mask_id;

@@ -358,7 +358,7 @@ def test_select_tiny_teacher_forced(dev):
         _check_step(ref, st, outs)
 
 
-@pytest.mark.parametrize("B,W,V", [(8, 16, 4096), (3, 64, 1003), (2, 5, 1)])
+@pytest.mark.parametrize("B,W,V", [(8, 16, 4096), (3, 64, 1003), (2, 5, 1), (4, 16, 16388), (2, 8, 40000), (1, 4, 16386)])
 def test_select_stream_small_free_running(B, W, V, dev):
     cfg = wl.SelectConfig("s", B=B, W=W, V=V, seed=4242 + V, alpha=0.25, tau=float(np.log(V) * 0.8) if V > 1 else 1.0,
                           steps=48, kind="mixture")
