@@ -174,6 +174,34 @@ def select_commit(logits: np.ndarray, tok, filled, pos, ctx_len, alpha: float, t
                 committed=committed, argmax=am, entropy=ent, margin=margin)
 
 
+def lmhead_logits(hidden: np.ndarray, lm_head: np.ndarray) -> np.ndarray:
+    """Logits of the LM head: z[..., v] = sum_k hidden[..., k] * lm_head[v, k]
+    in float64 (numpy's matmul as the contraction).  The inputs are the
+    stored values (bf16 read as float64).
+
+    The LM head is the backbone's output projection: it maps a slot's final
+    hidden state to the vocabulary logits whose softmax the select step
+    scores (WeDLM paper-summary page, "Method", inference paragraph: masked
+    slots are predicted from the model's output distribution; the backbone
+    is Qwen3-8B, TL;DR)."""
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(lm_head, dtype=np.float64)
+    if h.shape[-1] != w.shape[1]:
+        raise ValueError("hidden size mismatch")
+    return h @ w.T
+
+
+def lmhead_select_commit(hidden: np.ndarray, lm_head: np.ndarray, tok, filled, pos, ctx_len,
+                         alpha: float, tau: float, mask_id: int):
+    """select_commit on the LM head's logits.  The fused kernel never stores
+    logits; its fp32 accumulators are taken here as the float64 logits
+    rounded to fp32 (the storage point of a logit)."""
+    z = lmhead_logits(hidden, lm_head).astype(np.float32)
+    out = select_commit(z, tok, filled, pos, ctx_len, alpha, tau, mask_id)
+    out["logits"] = z
+    return out
+
+
 def decode_step_attention(inp, scale: Optional[float] = None, rows=None):
     """Oracle for reorder + attention on one batch drawn by
     workloads.make_attn_inputs.  Returns a dict

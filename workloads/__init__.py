@@ -23,6 +23,14 @@ follow the Qwen3-8B backbone named in the WeDLM paper summary, TL;DR):
                    vocabulary; each row is low-entropy (N(0,1) with one
                    uniformly chosen index set to 12.0) or high-entropy
                    (N(0,1)) with probability 1/2 each.
+* ``lmhead_v152k`` the same window and vocabulary with the logits produced
+                   on the fly by the LM head: hidden states [64, 16, 4096]
+                   and an output-embedding matrix [151936, 4096], both bf16
+                   (Qwen3-8B's hidden size and vocabulary).  Weights are
+                   N(0, 1/4096); a hidden row is N(0,1) noise (logits about
+                   N(0,1)), and with probability 1/2 it also gets
+                   12 w_k / |w_k|^2 for a uniformly chosen token k, which
+                   lifts logit k by 12 (the low-entropy rows).
 
 Values are N(0,1) unless stated.  bf16 storage is the round-to-nearest-even
 cast of the fp32 draw; the returned arrays hold the raw 16-bit patterns
@@ -85,6 +93,29 @@ CONFIGS: Dict[str, object] = {
     "long_b4": AttnConfig("long_b4", B=4, W=32, Hq=32, Hkv=8, D=128, dtype="bf16",
                           rope_base=1e6, seed=1004, L=32768, n_obs=16),
 }
+
+@dataclass(frozen=True)
+class LmheadConfig:
+    name: str
+    B: int
+    W: int
+    Dm: int      # hidden size
+    V: int
+    seed: int
+    alpha: float
+    tau: float
+    steps: int
+
+
+LMHEAD_CONFIGS: Dict[str, LmheadConfig] = {
+    "lmhead_small": LmheadConfig("lmhead_small", B=2, W=8, Dm=256, V=3000, seed=1101, alpha=0.25,
+                                 tau=float(np.log(3000) * 0.8), steps=24),
+    "lmhead_mid": LmheadConfig("lmhead_mid", B=12, W=16, Dm=1024, V=40000, seed=1102, alpha=0.25,
+                               tau=float(np.log(40000) * 0.8), steps=6),
+    "lmhead_v152k": LmheadConfig("lmhead_v152k", B=64, W=16, Dm=4096, V=151936, seed=1105, alpha=0.25,
+                                 tau=9.0, steps=256),
+}
+
 
 SELECT_CONFIGS: Dict[str, SelectConfig] = {
     "tiny_f32": SelectConfig("tiny_f32", B=1, W=8, V=1000, seed=1001, alpha=0.25, tau=4.5,
@@ -308,6 +339,63 @@ def make_logits_torch(cfg: SelectConfig, step: int, device, out=None):
         cur = rows.gather(1, flat_idx)
         rows.scatter_(1, flat_idx, torch.where(spike.view(-1, 1), torch.full_like(cur, 12.0), cur))
     return out
+
+
+# ----------------------------------------------------------------------------
+# LM-head inputs (hidden states and output embeddings, bf16)
+# ----------------------------------------------------------------------------
+def make_lm_head_np(cfg: LmheadConfig) -> np.ndarray:
+    """Output-embedding matrix [V, Dm], N(0, 1/Dm), as bf16 bits."""
+    rng = np.random.default_rng(cfg.seed)
+    w = _normal(rng, (cfg.V, cfg.Dm))
+    w *= np.float32(1.0 / np.sqrt(cfg.Dm))
+    return f32_to_bf16_bits(w)
+
+
+def make_hidden_np(cfg: LmheadConfig, step: int, lm_head_bits: np.ndarray,
+                   B: Optional[int] = None) -> np.ndarray:
+    """Hidden states [B, W, Dm] of one step as bf16 bits (seed = cfg.seed +
+    1000 + step): N(0,1) rows; with probability 1/2 a row also gets
+    12 w_k / |w_k|^2 for a uniformly drawn token k (w_k = row k of the
+    stored output embeddings), which lifts its logit k by about 12."""
+    B = cfg.B if B is None else B
+    rng = np.random.default_rng(cfg.seed + 1000 + step)
+    h = _normal(rng, (B, cfg.W, cfg.Dm))
+    low = rng.random((B, cfg.W)) < 0.5
+    idx = rng.integers(0, cfg.V, size=(B, cfg.W))
+    bi, wi = np.nonzero(low)
+    if len(bi):
+        wk = bf16_bits_to_f32(lm_head_bits[idx[bi, wi]])
+        h[bi, wi] += np.float32(12.0) * wk / np.sum(wk * wk, axis=1, keepdims=True)
+    return f32_to_bf16_bits(h)
+
+
+def make_lm_head_torch(cfg: LmheadConfig, device):
+    """Device draw of the [V, Dm] bf16 output embeddings (torch's generator,
+    seed = cfg.seed; same recipe as make_lm_head_np, other random stream)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+    w = torch.empty((cfg.V, cfg.Dm), dtype=torch.float32, device=device)
+    w.normal_(generator=g)
+    w.mul_(1.0 / float(np.sqrt(cfg.Dm)))
+    return w.to(torch.bfloat16)
+
+
+def make_hidden_torch(cfg: LmheadConfig, step: int, lm_head, device):
+    """Device draw of one step's [B, W, Dm] bf16 hidden states (recipe of
+    make_hidden_np, torch's generator, seed = cfg.seed + 1000 + step)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed + 1000 + step)
+    h = torch.empty((cfg.B, cfg.W, cfg.Dm), dtype=torch.float32, device=device)
+    h.normal_(generator=g)
+    low = torch.rand((cfg.B, cfg.W), generator=g, device=device) < 0.5
+    idx = torch.randint(0, cfg.V, (cfg.B, cfg.W), generator=g, device=device)
+    wk = lm_head[idx.view(-1)].float().view(cfg.B, cfg.W, cfg.Dm)
+    spike = 12.0 * wk / (wk * wk).sum(dim=-1, keepdim=True)
+    h += torch.where(low[..., None], spike, torch.zeros_like(spike))
+    return h.to(torch.bfloat16)
 
 
 # ----------------------------------------------------------------------------
