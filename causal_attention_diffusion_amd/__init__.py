@@ -19,12 +19,15 @@ from .binding import (  # noqa: F401
     WedlmError,
     attn_plan,
     lib_path,
+    lmhead_workspace_tensor,
     load_library,
     make_shape,
     select_workspace_tensor,
     attn_workspace_tensor,
     wedlm_attn_plan,
     wedlm_last_error,
+    wedlm_lmhead_select_commit,
+    wedlm_lmhead_select_commit_workspace,
     wedlm_reorder,
     wedlm_select_commit,
     wedlm_select_commit_workspace,

@@ -54,6 +54,11 @@ def load_library():
     lib.wedlm_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P,
                                         C.c_float, C.c_float, i32, P, sz, P]
     lib.wedlm_select_commit.restype = C.c_int
+    lib.wedlm_lmhead_select_commit_workspace.argtypes = [i32, i32, i32, i32]
+    lib.wedlm_lmhead_select_commit_workspace.restype = sz
+    lib.wedlm_lmhead_select_commit.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                               C.c_float, C.c_float, i32, P, sz, P]
+    lib.wedlm_lmhead_select_commit.restype = C.c_int
     lib.wedlm_attn_plan.argtypes = [S, i32, C.POINTER(i32), C.POINTER(i32)]
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
@@ -228,6 +233,49 @@ def wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit, committed, 
         B, W, V, _ptr(logits), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len), _ptr(n_commit),
         _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), float(alpha), float(tau), int(mask_id),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wedlm_lmhead_select_commit_workspace(B: int, W: int, V: int, Dm: int) -> int:
+    return int(load_library().wedlm_lmhead_select_commit_workspace(int(B), int(W), int(V), int(Dm)))
+
+
+def lmhead_workspace_tensor(B: int, W: int, V: int, Dm: int, device):
+    """Workspace for wedlm_lmhead_select_commit (no initialisation needed)."""
+    import torch
+    n = wedlm_lmhead_select_commit_workspace(B, W, V, Dm)
+    if n == 0:
+        raise WedlmError(f"unsupported LM-head shape B={B} W={W} V={V} Dm={Dm}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def wedlm_lmhead_select_commit(hidden, lm_head, tok, filled, pos, ctx_len, n_commit, committed,
+                               alpha: float, tau: float, mask_id: int, workspace, argmax_out=None,
+                               entropy_out=None, stream=None):
+    """hidden [B, W, Dm] and lm_head [V, Dm] bfloat16 tensors; window state
+    and outputs as for wedlm_select_commit."""
+    import torch
+    if hidden.dim() != 3 or hidden.dtype != torch.bfloat16 or not hidden.is_contiguous():
+        raise WedlmError("hidden must be a contiguous [B, W, Dm] bfloat16 tensor")
+    B, W, Dm = hidden.shape
+    if lm_head.dim() != 2 or lm_head.dtype != torch.bfloat16 or lm_head.shape[1] != Dm \
+            or not lm_head.is_contiguous():
+        raise WedlmError("lm_head must be a contiguous [V, Dm] bfloat16 tensor")
+    V = lm_head.shape[0]
+    _expect(tok, "tok", (B, W), torch.int32)
+    _expect(filled, "filled", (B, W), torch.uint8)
+    _expect(pos, "pos", (B, W), torch.int32)
+    _expect(ctx_len, "ctx_len", (B,), torch.int32)
+    _expect(n_commit, "n_commit", (B,), torch.int32)
+    _expect(committed, "committed", (B, W), torch.int32)
+    _opt(argmax_out, "argmax_out", (B, W), torch.int32)
+    _opt(entropy_out, "entropy_out", (B, W), torch.float32)
+    if workspace is None or workspace.dtype != torch.uint8:
+        raise WedlmError("workspace must be a uint8 tensor (lmhead_workspace_tensor)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().wedlm_lmhead_select_commit(
+        B, W, V, Dm, _ptr(hidden), _ptr(lm_head), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len),
+        _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), float(alpha), float(tau),
+        int(mask_id), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def wedlm_last_error() -> str:

@@ -141,6 +141,72 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     return p;
 }
 
+// ---------------------------------------------------------------- LM head + select / commit
+struct LmheadLayout {
+    size_t rows, count, part, row_stat, total;
+    int nvt, nrg;
+};
+
+static bool lmhead_layout(int32_t B, int32_t W, int32_t V, int32_t Dm, LmheadLayout* L) {
+    if (B < 1 || W < 1 || W > 64 || (int64_t)B * W > 4096 || V < 1 || Dm < kLmKC || Dm > 65536 ||
+        Dm % kLmKC != 0)
+        return false;
+    const int64_t R = (int64_t)B * W;
+    L->nvt = (int)((V + kLmNT - 1) / kLmNT);
+    L->nrg = (int)((R + kLmMT - 1) / kLmMT);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    L->rows = 0;
+    L->count = up((size_t)R * 4);
+    L->part = L->count + 256;
+    L->row_stat = L->part + up((size_t)R * L->nvt * sizeof(float4));
+    L->total = L->row_stat + up((size_t)R * sizeof(float4));
+    return true;
+}
+
+extern "C" size_t wedlm_lmhead_select_commit_workspace(int32_t B, int32_t W, int32_t V, int32_t Dm) {
+    LmheadLayout L;
+    return lmhead_layout(B, W, V, Dm, &L) ? L.total : 0;
+}
+
+extern "C" int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32_t Dm, const void* hidden,
+                                          const void* lm_head, int32_t* tok, uint8_t* filled, int32_t* pos,
+                                          int32_t* ctx_len, int32_t* n_commit, int32_t* committed,
+                                          int32_t* argmax_out, float* entropy_out, float alpha, float tau,
+                                          int32_t mask_id, void* workspace, size_t ws_bytes, void* stream) {
+    LmheadLayout L;
+    if (!lmhead_layout(B, W, V, Dm, &L))
+        return fail(WEDLM_ERR_SHAPE,
+                    "need B >= 1, 1 <= W <= 64, B*W <= 4096, V >= 1, Dm a multiple of %d in [%d, 65536] "
+                    "(B=%d W=%d V=%d Dm=%d)", kLmKC, kLmKC, B, W, V, Dm);
+    if (!hidden || !lm_head || !tok || !filled || !pos || !ctx_len || !n_commit || !committed)
+        return fail(WEDLM_ERR_ARG, "wedlm_lmhead_select_commit: NULL device pointer");
+    if (reinterpret_cast<uintptr_t>(hidden) % 16 || reinterpret_cast<uintptr_t>(lm_head) % 16)
+        return fail(WEDLM_ERR_ARG, "hidden and lm_head must be 16-byte aligned");
+    if (!isfinite(alpha) || !isfinite(tau)) return fail(WEDLM_ERR_ARG, "alpha and tau must be finite");
+    if (!workspace || ws_bytes < L.total)
+        return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace ? ws_bytes : 0);
+    char* ws = static_cast<char*>(workspace);
+    LmheadArgs g;
+    g.hidden = static_cast<const bf16_t*>(hidden);
+    g.lm_head = static_cast<const bf16_t*>(lm_head);
+    g.filled = filled;
+    g.rows = reinterpret_cast<int32_t*>(ws + L.rows);
+    g.count = reinterpret_cast<int32_t*>(ws + L.count);
+    g.part = reinterpret_cast<float4*>(ws + L.part);
+    g.row_stat = reinterpret_cast<float4*>(ws + L.row_stat);
+    g.R = B * W; g.Dm = Dm; g.V = V; g.nvt = L.nvt; g.nrg = L.nrg;
+    hipStream_t st = (hipStream_t)stream;
+    int rc = hip_status(launch_lmhead(g, st), "wedlm_lmhead_select_commit launch");
+    if (rc != WEDLM_OK) return rc;
+    SelectArgs a;
+    a.logits = nullptr; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
+    a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;
+    a.part = g.row_stat;
+    a.B = B; a.W = W; a.V = V; a.nparts = 1; a.part_len = V;
+    a.alpha = alpha; a.tau = tau; a.mask_id = mask_id;
+    return hip_status(launch_commit(a, st), "wedlm_lmhead_select_commit launch");
+}
+
 extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_t* nsplit, int32_t* split_keys) {
     int rc = check_shape(s);
     if (rc) return rc;

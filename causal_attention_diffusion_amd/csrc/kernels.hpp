@@ -59,6 +59,20 @@ struct SelectArgs {
     int mask_id;
 };
 
+struct LmheadArgs {
+    const bf16_t* hidden;   // [R][Dm], R = B*W rows in (b, j) order
+    const bf16_t* lm_head;  // [V][Dm]
+    const uint8_t* filled;  // [R]
+    int32_t* rows;          // workspace [R]: global row of each masked row, in order
+    int32_t* count;         // workspace: number of masked rows
+    float4* part;           // workspace [R][nvt]: (m, argmax bits, S, T) per masked row and vocab tile
+    float4* row_stat;       // workspace [R]: merged statistics of each masked row (by global row)
+    int R, Dm, V, nvt, nrg;  // nvt vocab tiles of kLmNT, nrg row groups of kLmMT
+};
+constexpr int kLmNT = 256;  // vocabulary entries per LM-head work-group
+constexpr int kLmMT = 128;  // masked rows per LM-head work-group
+constexpr int kLmKC = 64;   // hidden-size elements per pipeline stage
+
 // Keys per split of one sequence: its visible keys T_len spread evenly over
 // the grid's nsplit work-groups, rounded up to the ring stage `align` and
 // never above split_keys (the host sized split_keys * nsplit for the longest
@@ -75,5 +89,8 @@ hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
 int attn_chunk(int dtype, int nw);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
+// commit / Eq. 11 select / refill alone, on row partials already in a.part
+hipError_t launch_commit(const SelectArgs& a, hipStream_t stream);
 
 }  // namespace wedlm

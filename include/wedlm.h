@@ -203,6 +203,45 @@ int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float *logits, in
                         size_t ws_bytes, void *stream);
 
 /*
+ * wedlm_lmhead_select_commit_workspace -- bytes of device workspace for
+ * wedlm_lmhead_select_commit at (B, W, V, Dm): the masked-row list, one
+ * 16-byte partial per (masked row, 256-entry vocabulary tile) and one per
+ * row.  0 if the shape is not supported.  Contents need no initialisation
+ * and are not preserved; calls that run at the same time must not share
+ * one workspace.
+ */
+size_t wedlm_lmhead_select_commit_workspace(int32_t B, int32_t W, int32_t V, int32_t Dm);
+
+/*
+ * wedlm_lmhead_select_commit -- the LM head fused with the select step.
+ * (paper-summary page, "Method", inference paragraph: masked slots are
+ * scored by the entropy of the model's predictive distribution and filled
+ * with its most likely token; TL;DR: the backbone is Qwen3-8B, hidden size
+ * 4096, vocabulary 151936.)
+ *
+ * Same as wedlm_select_commit with
+ *     logits[b][j][v] = sum_k hidden[b][j][k] * lm_head[v][k]
+ * taken from bf16 operands with fp32 accumulation (MFMA) and folded into the
+ * per-slot statistics as they are produced: no logit is written.  Only the
+ * masked slots' rows are computed.
+ *
+ *   hidden   [B][W][Dm] bf16 device, the window's final hidden states in
+ *            logical slot order (16-byte aligned)
+ *   lm_head  [V][Dm] bf16 device, row v = output embedding of token v
+ *            (16-byte aligned)
+ *   other arguments as for wedlm_select_commit; workspace / ws_bytes see
+ *   wedlm_lmhead_select_commit_workspace.
+ * Dm: a multiple of 64, 64..65536.  B*W <= 4096, W <= 64, V >= 1.
+ * Errors: WEDLM_ERR_SHAPE / WEDLM_ERR_ARG / WEDLM_ERR_WORKSPACE before any
+ * launch; WEDLM_ERR_HIP if a launch fails.
+ */
+int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32_t Dm, const void *hidden,
+                               const void *lm_head, int32_t *tok, uint8_t *filled, int32_t *pos,
+                               int32_t *ctx_len, int32_t *n_commit, int32_t *committed,
+                               int32_t *argmax_out, float *entropy_out, float alpha, float tau,
+                               int32_t mask_id, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for
  * this shape and bound: work-groups per (sequence, KV head, row tile)
  * (*nsplit) and keys per work-group (*split_keys).  Either may be NULL.

@@ -186,3 +186,23 @@ def test_product_and_oracle_share_no_code():
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "causal_attention_diffusion_amd" not in text, f
             assert not re.search(r'#include\s+"[^"]*(csrc|include/wedlm)', text), f
+
+
+def test_lmhead_validation_and_workspace():
+    lib = wd.load_library()
+    fake = C.c_void_p(0x1000)
+    ws = lib.wedlm_lmhead_select_commit_workspace
+    assert ws(64, 16, 151936, 4096) > 64 * 16 * 594 * 16
+    assert ws(1, 1, 1, 64) > 0
+    for bad in [(0, 16, 100, 64), (1, 65, 100, 64), (65, 64, 100, 64), (1, 8, 0, 64), (1, 8, 100, 96),
+                (1, 8, 100, 0), (1, 8, 100, 65536 + 64)]:
+        assert ws(*bad) == 0, bad
+    args = [fake] * 10 + [C.c_float(0.1), C.c_float(1.0), 100, fake, C.c_size_t(1 << 30), None]
+    assert lib.wedlm_lmhead_select_commit(1, 8, 100, 96, *args) == ERR_SHAPE
+    assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, None, *args[1:]) == ERR_ARG
+    misaligned = C.c_void_p(0x1008)
+    assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, misaligned, *args[1:]) == ERR_ARG
+    small = args[:14] + [C.c_size_t(ws(1, 8, 100, 64) - 1), None]
+    assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, *small) == ERR_WS
+    nan = args[:10] + [C.c_float(float("nan"))] + args[11:]
+    assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, *nan) == ERR_ARG
