@@ -52,9 +52,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_b4",
-                    choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32", "select_v152k"],
+                    choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32", "select_v152k",
+                             "lmhead_v152k"],
                     help="select_v152k times the select/commit call alone (batch 64 x window 16, "
-                         "V=151936, streaming from an all-masked window)")
+                         "V=151936, streaming from an all-masked window); lmhead_v152k the fused "
+                         "LM head + select call (hidden 4096) on the same window")
     ap.add_argument("--vocab", type=int, default=151936)
     ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
@@ -99,6 +101,9 @@ def main():
 
     if args.workload == "select_v152k":
         bench_select(args)
+        return
+    if args.workload == "lmhead_v152k":
+        bench_lmhead(args)
         return
 
     import torch
@@ -406,6 +411,132 @@ def bench_select(args):
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_select(cfg, args)
     print(json.dumps(result), flush=True)
+
+
+def bench_lmhead(args):
+    """The fused LM head + select call alone, streaming: batch 64 x window 16,
+    hidden size 4096, V=151936 (Qwen3-8B's output projection), from an
+    all-masked window.  Step i reads hidden-state buffer i mod --logit-ring
+    (seeded device draws); the output embeddings are one seeded draw."""
+    import torch
+    import workloads as wl
+    import causal_attention_diffusion_amd as wd
+
+    dev = torch.device("cuda:0")
+    cfg = wl.LMHEAD_CONFIGS["lmhead_v152k"]
+    B, W, V, Dm = cfg.B, cfg.W, cfg.V, cfg.Dm
+    total = args.warmup + args.steps
+    w = wl.make_lm_head_torch(cfg, dev)
+    hidden = [wl.make_hidden_torch(cfg, i, w, dev) for i in range(args.logit_ring)]
+    ws = wd.lmhead_workspace_tensor(B, W, V, Dm, dev)
+    init = [torch.from_numpy(x).to(dev) for x in wl.initial_window(B, W, V)]
+    tok, filled, pos, ctx = [x.clone() for x in init]
+    n_commit_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    committed = torch.empty((B, W), dtype=torch.int32, device=dev)
+    argmax_hist = torch.empty((total, B, W), dtype=torch.int32, device=dev)
+
+    def step(i):
+        wd.wedlm_lmhead_select_commit(hidden[i % len(hidden)], w, tok, filled, pos, ctx, n_commit_hist[i],
+                                      committed, cfg.alpha, cfg.tau, V, ws, argmax_out=argmax_hist[i])
+
+    def reset():
+        for x, y in zip((tok, filled, pos, ctx), init):
+            x.copy_(y)
+
+    for i in range(args.warmup):
+        step(i)
+    reset()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.warmup, total):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    eager_elapsed = time.perf_counter() - t0
+    call_ms = ev0.elapsed_time(ev1) / args.steps
+    state_eager = [x.clone() for x in (tok, filled, pos, ctx)]
+    elapsed = eager_elapsed
+    if not args.eager:
+        reset()
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.warmup, total):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(2):
+            reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+        for x, y in zip((tok, filled, pos, ctx), state_eager):
+            if not torch.equal(x, y):
+                print("graph replay diverged from the eager steps", file=sys.stderr)
+                sys.exit(3)
+
+    K = args.steps
+    ms_step = elapsed * 1e3 / K
+    masked = (argmax_hist[args.warmup:] >= 0).sum(dim=(1, 2)).cpu().numpy().astype(np.int64)
+    nc = n_commit_hist[args.warmup:].cpu().numpy().astype(np.int64)
+    # algorithmic work per call: 2 Dm flops per (masked row, vocabulary entry);
+    # bytes: the output embeddings once plus the masked rows' hidden states
+    flops = 2.0 * float(masked.mean()) * Dm * V
+    alg_bytes = float(V) * Dm * 2 + float(masked.mean()) * Dm * 2
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(B * W / (ms_step * 1e-3), 1),
+        "unit": "window tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "graph": not args.eager,
+        "eager_ms_per_step": round(eager_elapsed * 1e3 / K, 4),
+        "config": {"workload": f"lmhead_v152k: B={B} W={W} hidden={Dm} vocab={V} bf16 LM head fused with "
+                               f"select/commit (alpha={cfg.alpha} tau={cfg.tau}), {K} streaming steps from "
+                               f"an all-masked window",
+                   "batch": B, "window": W, "hidden": Dm, "vocab": V, "hidden_buffers": len(hidden)},
+        "steps_per_s": round(1e3 / ms_step, 2),
+        "lmhead_select_commit": {"avg_ms": round(call_ms, 5), "masked_rows_per_step": round(float(masked.mean()), 2),
+                                 "alg_flops_per_launch": int(flops), "TFLOP_per_s": round(tflops, 1),
+                                 "weights_GB_per_s": round(alg_bytes / (call_ms * 1e-3) / 1e9, 1),
+                                 "logits_bytes_not_written_per_step": int(masked.mean() * V * 4)},
+        "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
+        "P_c": round(float(nc.sum()) / (K * B * W), 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "kernel": "wedlm_lmhead_select_commit (lmhead_stats + merge + commit)"},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_lmhead(cfg, args, w, hidden[0])
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_lmhead(cfg, args, w_dev, h_dev):
+    """The oracle's LM head + select step, untuned, on the host cores, for one
+    sequence of the all-masked first step (16 rows x 151936 x 4096), on the
+    bench's own bf16 inputs copied to the host."""
+    import oracle
+    import workloads as wl
+    w64 = w_dev.float().cpu().numpy().astype(np.float64)
+    h64 = h_dev[:1].float().cpu().numpy().astype(np.float64)
+    tok, filled, pos, ctx = wl.initial_window(1, cfg.W, cfg.V)
+    reps, dt_s = 0, 0.0
+    while reps < 64 and dt_s < 10.0:
+        t0 = time.perf_counter()
+        oracle.lmhead_select_commit(h64, w64, tok, filled, pos, ctx, cfg.alpha, cfg.tau, cfg.V)
+        dt_s += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(reps * cfg.W / dt_s, 2), "unit": "window tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"1 of {cfg.B} sequences of the first step ({cfg.W} masked rows, hidden {cfg.Dm}, "
+                      f"V={cfg.V}) repeated {reps}x; {dt_s:.2f} s"}
 
 
 def cpu_baseline_select(cfg, args):

@@ -67,11 +67,11 @@ struct LmheadArgs {
     int32_t* count;         // workspace: number of masked rows
     float4* part;           // workspace [R][nvt]: (m, argmax bits, S, T) per masked row and vocab tile
     float4* row_stat;       // workspace [R]: merged statistics of each masked row (by global row)
-    int R, Dm, V, nvt, nrg;  // nvt vocab tiles of kLmNT, nrg row groups of kLmMT
+    int R, Dm, V, nvt, nrg;  // nvt vocab tiles of kLmNT; nrg row groups (set by the launcher)
 };
 constexpr int kLmNT = 256;  // vocabulary entries per LM-head work-group
-constexpr int kLmMT = 128;  // masked rows per LM-head work-group
-constexpr int kLmKC = 64;   // hidden-size elements per pipeline stage
+constexpr int kLmMT = 128;  // masked rows per LM-head work-group of the small-window shape
+constexpr int kLmKC = 64;   // the hidden size must be a multiple of this
 
 // Keys per split of one sequence: its visible keys T_len spread evenly over
 // the grid's nsplit work-groups, rounded up to the ring stage `align` and

@@ -14,18 +14,17 @@
 //   lmhead_rows   lists the masked rows of the window (only those are
 //                 scored: filled slots need no prediction);
 //   lmhead_stats  one work-group per (vocabulary tile of kLmNT entries,
-//                 group of kLmMT masked rows): C^T = W_tile H_group^T over
-//                 the hidden size in stages of kLmKC, then the tile's
-//                 statistics per row;
+//                 group of masked rows): C^T = W_tile H_group^T over the
+//                 hidden size in stages, then the tile's statistics per row;
 //   lmhead_merge  one wave per masked row merges its tiles' statistics;
 //   commit_select_refill (select.hip) then runs commit / Eq. 11 / refill
 //                 on the merged rows exactly as after vocab_stats.
 //
 // lmhead_stats streams both operands through LDS with direct global->LDS
 // loads (global_load_lds_dwordx4, 1 KB per wave instruction) in a ring of
-// kAhead+1 stages, like the attention kernel.  Row slices are 128 bytes;
-// the 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so the fragment
-// reads (32 rows x one chunk per half-wave) hit distinct banks.  The MFMA is
+// stages, like the attention kernel.  The 16-byte chunks of a row slice are
+// XOR-swizzled (LmCfg::swz) so the fragment reads (32 rows x one chunk per
+// half-wave) hit distinct banks.  The MFMA is
 // v_mfma_f32_32x32x16_bf16 with the vocabulary as its M side: a lane's 16
 // accumulators are 16 vocabulary entries of one hidden row, so the row
 // statistics are in-lane plus one exchange with lane ^ 32.
@@ -35,18 +34,32 @@
 namespace wedlm {
 
 namespace {
-constexpr int kNW = 8;                            // waves per work-group: 4 (vocab) x 2 (rows)
-constexpr int kAhead = 2;                         // stages in flight beyond the one computed
-constexpr int kSlots = kAhead + 1;
-constexpr int kRowB = kLmKC * 2;                  // bytes of one row in a stage (128)
-constexpr int kABytes = kLmNT * kRowB;            // weight rows of a stage (32 KB)
-constexpr int kBBytes = kLmMT * kRowB;            // hidden rows of a stage (16 KB)
-constexpr int kSlotB = kABytes + kBBytes;
-constexpr int kLPS = kSlotB / 1024 / kNW;         // DMA instructions per wave per stage (6)
-static_assert(kLPS * 1024 * kNW == kSlotB, "a stage must split into whole wave loads");
-static_assert(kRowB == 128, "the chunk swizzle assumes 8 chunks per row");
+constexpr int kNW = 8;   // waves per work-group
 
-__device__ __forceinline__ int lm_swz(int row, int c) { return c ^ ((row >> 1) & 7); }
+// Tile shape of lmhead_stats: NT vocabulary entries x MT masked rows per
+// work-group, waves WN (vocabulary) x 8/WN (rows), the hidden size in stages
+// of KC, SLOTS stages of LDS (SLOTS - 1 in flight beyond the one computed).
+template <int NT_, int MT_, int KC_, int SLOTS_, int WN_>
+struct LmCfg {
+    static constexpr int NT = NT_, MT = MT_, KC = KC_, SLOTS = SLOTS_, WN = WN_, WM = kNW / WN_;
+    static constexpr int AHEAD = SLOTS - 1;
+    static constexpr int RB = KC * 2;                 // bytes of one row in a stage
+    static constexpr int CPR = KC / 8;                // 16-byte chunks per row
+    static constexpr int RPI = 1024 / RB;             // rows per 1 KB wave load
+    static constexpr int ABYTES = NT * RB, BBYTES = MT * RB, SLOTB = ABYTES + BBYTES;
+    static constexpr int LPS = (NT + MT) / RPI / kNW; // DMA instructions per wave per stage
+    static constexpr int TN = NT / WN / 32, TM = MT / WM / 32;   // 32-tiles per wave
+    static_assert(LPS * RPI * kNW == NT + MT, "a stage must split into whole wave loads");
+    static_assert(NT % RPI == 0 && TN >= 1 && TM >= 1 && CPR >= 2, "tile shape");
+    static_assert(SLOTS * SLOTB <= 160 * 1024 - 4096, "LDS");
+    // chunk c of row r sits at c ^ g(r): 16 consecutive rows (one half-wave
+    // reading one chunk each) land on 16 distinct 16-byte bank groups
+    __device__ static int swz(int row, int c) { return c ^ ((row / (256 / RB)) & (CPR - 1)); }
+};
+// up to 128 window rows: the weights stream once, HBM-bound
+using LmSmall = LmCfg<256, kLmMT, 64, 3, 4>;
+// more rows: 256-row groups, waves of 128 x 64 (8 MFMAs per fragment set)
+using LmLarge = LmCfg<256, 2 * kLmMT, 32, 4, 2>;
 
 template <int N>
 __device__ __forceinline__ void lm_wait_vm() {
@@ -88,9 +101,10 @@ __global__ __launch_bounds__(256) void lmhead_rows(LmheadArgs a) {
     if (t == 255) *a.count = s_cnt[255];
 }
 
+template <class C>
 __global__ __launch_bounds__(512) void lmhead_stats(LmheadArgs a) {
-    __shared__ __attribute__((aligned(1024))) char s_ring[kSlots * kSlotB];
-    __shared__ int s_rows[kLmMT];
+    __shared__ __attribute__((aligned(1024))) char s_ring[C::SLOTS * C::SLOTB];
+    __shared__ int s_rows[C::MT];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,133 +118,137 @@ __global__ __launch_bounds__(512) void lmhead_stats(LmheadArgs a) {
     const int vt = (j / a.nrg) * 8 + xcd;
     if (vt >= a.nvt) return;
     const int cnt = *a.count;
-    const int c0 = rg * kLmMT;
+    const int c0 = rg * C::MT;
     if (c0 >= cnt) return;
-    if (tid < kLmMT) s_rows[tid] = a.rows[min(c0 + tid, cnt - 1)];   // rows past the count repeat a valid one
+    if (tid < C::MT) s_rows[tid] = a.rows[min(c0 + tid, cnt - 1)];   // rows past the count repeat a valid one
     __syncthreads();
-    const int n0 = vt * kLmNT;
-    const int ns = a.Dm / kLmKC;
+    const int n0 = vt * C::NT;
+    const int ns = a.Dm / C::KC;
     const size_t rowbytes = (size_t)a.Dm * 2;
 
-    // DMA sources of this lane: instruction q of a stage loads 8 row slices
-    // (weights for q < kLmNT/8, then hidden rows); the lane that fills LDS
-    // chunk (row, lane & 7) reads global chunk lm_swz(row, lane & 7).
-    const char* gsrc[kLPS];
-    uint32_t ldst[kLPS];
+    // DMA sources of this lane: instruction q of a stage loads RPI row slices
+    // (weights for q < NT/RPI, then hidden rows); the lane that fills LDS
+    // chunk (row, p) reads global chunk swz(row, p).
+    const char* gsrc[C::LPS];
+    uint32_t ldst[C::LPS];
 #pragma unroll
-    for (int u = 0; u < kLPS; ++u) {
-        const int q = w * kLPS + u;
-        if (q < kLmNT / 8) {
-            const int row = q * 8 + (lane >> 3);
+    for (int u = 0; u < C::LPS; ++u) {
+        const int q = w * C::LPS + u;
+        const int p = lane % C::CPR;
+        if (q < C::NT / C::RPI) {
+            const int row = q * C::RPI + lane / C::CPR;
             const int n = min(n0 + row, a.V - 1);   // past the vocabulary: a valid row, masked below
-            gsrc[u] = reinterpret_cast<const char*>(a.lm_head) + (size_t)n * rowbytes + lm_swz(row, lane & 7) * 16;
+            gsrc[u] = reinterpret_cast<const char*>(a.lm_head) + (size_t)n * rowbytes + C::swz(row, p) * 16;
             ldst[u] = q * 1024;
         } else {
-            const int m = (q - kLmNT / 8) * 8 + (lane >> 3);
-            gsrc[u] = reinterpret_cast<const char*>(a.hidden) + (size_t)s_rows[m] * rowbytes + lm_swz(m, lane & 7) * 16;
-            ldst[u] = kABytes + (q - kLmNT / 8) * 1024;
+            const int m = (q - C::NT / C::RPI) * C::RPI + lane / C::CPR;
+            gsrc[u] = reinterpret_cast<const char*>(a.hidden) + (size_t)s_rows[m] * rowbytes + C::swz(m, p) * 16;
+            ldst[u] = C::ABYTES + (q - C::NT / C::RPI) * 1024;
         }
     }
     auto issue = [&](int st) {
-        char* slot = s_ring + (st % kSlots) * kSlotB;
+        char* slot = s_ring + (st % C::SLOTS) * C::SLOTB;
 #pragma unroll
-        for (int u = 0; u < kLPS; ++u)
+        for (int u = 0; u < C::LPS; ++u)
             __builtin_amdgcn_global_load_lds(
-                (const void*)(gsrc[u] + (size_t)st * kRowB),
+                (const void*)(gsrc[u] + (size_t)st * C::RB),
                 (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(slot + ldst[u])), 16, 0, 0);
     };
 
-    // wave (wn, wm): vocabulary rows wn*64 .. +64 (two 32-tiles) x hidden
-    // rows wm*64 .. +64 (two 32-tiles)
-    const int wn = w & 3, wm = w >> 2;
+    // wave (wn, wm): vocabulary rows wn*TN*32 .. (TN 32-tiles) x hidden rows
+    // wm*TM*32 .. (TM 32-tiles)
+    const int wn = w % C::WN, wm = w / C::WN;
     const int hl = lane >> 5, col = lane & 31;
-    uint32_t aoff[2], boff[2];
-    int arow[2], brow[2];
+    int arow[C::TN], brow[C::TM];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        arow[t] = wn * 64 + t * 32 + col;
-        brow[t] = wm * 64 + t * 32 + col;
-        aoff[t] = arow[t] * kRowB;
-        boff[t] = kABytes + brow[t] * kRowB;
-    }
-    f32x16 acc[2][2];
+    for (int t = 0; t < C::TN; ++t) arow[t] = (wn * C::TN + t) * 32 + col;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int t = 0; t < C::TM; ++t) brow[t] = (wm * C::TM + t) * 32 + col;
+    f32x16 acc[C::TN][C::TM];
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+    for (int x = 0; x < C::TN; ++x)
+#pragma unroll
+        for (int y = 0; y < C::TM; ++y)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
 
-    const int npro = ns < kAhead ? ns : kAhead;
+    const int npro = ns < C::AHEAD ? ns : C::AHEAD;
     for (int st = 0; st < npro; ++st) issue(st);
     for (int st = 0; st < ns; ++st) {
-        // this wave's loads of stage st have landed (later stages may still
-        // be in flight); the barrier publishes every wave's part and frees
-        // the slot of stage st-1 for stage st+kAhead
-        if (st + 1 < ns) lm_wait_vm<kLPS * (kAhead - 1)>();
-        else lm_wait_vm<0>();
+        // this wave's loads of stage st have landed (up to AHEAD-1 later
+        // stages may still be in flight); the barrier publishes every wave's
+        // part and frees the slot of stage st-1 for stage st+AHEAD
+        switch (min(C::AHEAD - 1, ns - 1 - st)) {
+            case 3: lm_wait_vm<3 * C::LPS>(); break;
+            case 2: lm_wait_vm<2 * C::LPS>(); break;
+            case 1: lm_wait_vm<C::LPS>(); break;
+            default: lm_wait_vm<0>(); break;
+        }
         lm_block_sync();
-        if (st + kAhead < ns) issue(st + kAhead);
-        const char* slot = s_ring + (st % kSlots) * kSlotB;
+        if (st + C::AHEAD < ns) issue(st + C::AHEAD);
+        const char* slot = s_ring + (st % C::SLOTS) * C::SLOTB;
 #pragma unroll
-        for (int s = 0; s < kLmKC / 16; ++s) {
-            bf16x8 af[2], bf[2];
+        for (int s = 0; s < C::KC / 16; ++s) {
+            bf16x8 af[C::TN], bf[C::TM];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                af[t] = *reinterpret_cast<const bf16x8*>(slot + aoff[t] + lm_swz(arow[t], 2 * s + hl) * 16);
-                bf[t] = *reinterpret_cast<const bf16x8*>(slot + boff[t] + lm_swz(brow[t], 2 * s + hl) * 16);
-            }
+            for (int t = 0; t < C::TN; ++t)
+                af[t] = *reinterpret_cast<const bf16x8*>(slot + arow[t] * C::RB + C::swz(arow[t], 2 * s + hl) * 16);
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
+            for (int t = 0; t < C::TM; ++t)
+                bf[t] = *reinterpret_cast<const bf16x8*>(slot + C::ABYTES + brow[t] * C::RB +
+                                                         C::swz(brow[t], 2 * s + hl) * 16);
 #pragma unroll
-                for (int y = 0; y < 2; ++y)
+            for (int x = 0; x < C::TN; ++x)
+#pragma unroll
+                for (int y = 0; y < C::TM; ++y)
                     acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[x], bf[y], acc[x][y], 0, 0, 0);
         }
     }
 
     // ---- statistics of this tile per hidden row
     lm_block_sync();   // every wave is done with the ring
-    float4* s_stat = reinterpret_cast<float4*>(s_ring);   // [4 vocab waves][kLmMT]
+    float4* s_stat = reinterpret_cast<float4*>(s_ring);   // [WN vocab waves][MT]
+    constexpr int NZ = C::TN * 16;
 #pragma unroll
-    for (int y = 0; y < 2; ++y) {
-        // the lane's 32 values in increasing vocabulary order: tile x, then
+    for (int y = 0; y < C::TM; ++y) {
+        // the lane's NZ values in increasing vocabulary order: tile x, then
         // accumulator e (entry (e / 4) * 8 + hl * 4 + e % 4 of the 32-tile)
-        float z[32];
+        float z[NZ];
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
+        for (int x = 0; x < C::TN; ++x)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int v = n0 + wn * 64 + x * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
+                const int v = n0 + (wn * C::TN + x) * 32 + (e >> 2) * 8 + hl * 4 + (e & 3);
                 z[x * 16 + e] = v < a.V ? acc[x][y][e] : -INFINITY;
             }
         float bm = z[0];
 #pragma unroll
-        for (int k = 1; k < 32; ++k) bm = fmaxf(bm, z[k]);
+        for (int k = 1; k < NZ; ++k) bm = fmaxf(bm, z[k]);
         Stat st{-INFINITY, 0x7fffffff, 0.f, 0.f};
         if (bm > -INFINITY) {
             int ba = 0x7fffffff;
 #pragma unroll
-            for (int k = 31; k >= 0; --k)   // backwards, so the first match wins
-                if (z[k] == bm) ba = n0 + wn * 64 + (k >> 4) * 32 + ((k & 15) >> 2) * 8 + hl * 4 + (k & 3);
+            for (int k = NZ - 1; k >= 0; --k)   // backwards, so the first match wins
+                if (z[k] == bm) ba = n0 + (wn * C::TN + (k >> 4)) * 32 + ((k & 15) >> 2) * 8 + hl * 4 + (k & 3);
             st.m = bm;
             st.a = ba;
         }
         float s = 0.f, t = 0.f;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) add_term(s, t, z[k], st.m);
+        for (int k = 0; k < NZ; ++k) add_term(s, t, z[k], st.m);
         st.s = s;
         st.t = t;
         st = merge(st, shfl_xor_stat(st, 32));
         if (hl == 0)
-            s_stat[wn * kLmMT + wm * 64 + y * 32 + col] = make_float4(st.m, __int_as_float(st.a), st.s, st.t);
+            s_stat[wn * C::MT + (wm * C::TM + y) * 32 + col] = make_float4(st.m, __int_as_float(st.a), st.s, st.t);
     }
     __syncthreads();
-    if (tid < kLmMT && c0 + tid < cnt) {
+    if (tid < C::MT && c0 + tid < cnt) {
         const float4 p0 = s_stat[tid];
         Stat o{p0.x, __float_as_int(p0.y), p0.z, p0.w};
 #pragma unroll
-        for (int k = 1; k < 4; ++k) {
-            const float4 p = s_stat[k * kLmMT + tid];
+        for (int k = 1; k < C::WN; ++k) {
+            const float4 p = s_stat[k * C::MT + tid];
             o = merge(o, Stat{p.x, __float_as_int(p.y), p.z, p.w});
         }
         a.part[(size_t)(c0 + tid) * a.nvt + vt] = make_float4(o.m, __int_as_float(o.a), o.s, o.t);
@@ -265,7 +283,15 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned nvt8 = (unsigned)((a.nvt + 7) / 8);
-    hipLaunchKernelGGL(lmhead_stats, dim3(8u * nvt8 * (unsigned)a.nrg), dim3(512), 0, st, a);
+    if (a.R <= LmSmall::MT) {
+        LmheadArgs b = a;
+        b.nrg = 1;
+        hipLaunchKernelGGL(lmhead_stats<LmSmall>, dim3(8u * nvt8), dim3(512), 0, st, b);
+    } else {
+        LmheadArgs b = a;
+        b.nrg = (a.R + LmLarge::MT - 1) / LmLarge::MT;
+        hipLaunchKernelGGL(lmhead_stats<LmLarge>, dim3(8u * nvt8 * (unsigned)b.nrg), dim3(512), 0, st, b);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_merge, dim3((unsigned)a.R), dim3(64), 0, st, a);
