@@ -202,6 +202,75 @@ def lmhead_select_commit(hidden: np.ndarray, lm_head: np.ndarray, tok, filled, p
     return out
 
 
+def dual_stream_visible(flags: np.ndarray, block: int) -> np.ndarray:
+    """Visibility of the Dual-Stream Masking attention for one sequence of N
+    tokens, as a [2N, 2N] boolean matrix over [memory stream ++ prediction
+    stream] in logical order (query row, key column).
+
+    WeDLM paper-summary page, "Method" (training paragraph) and "Key claims"
+    (sec. 4.2, Eq. 8-10): a clean memory stream and a block-masked prediction
+    stream share position ids; prediction tokens of block i attend to the
+    memory tokens whose logical positions precede block i.  Readings where
+    the page is silent: the memory stream is plainly causal; inside its own
+    block a prediction token follows Topological Reordering under the causal
+    mask (sec. 3.2, 4.1), i.e. token t sees token s of its block iff
+    (s observed and (t masked or s <= t)) or (both masked and s <= t); the
+    prediction stream sees no prediction token of another block."""
+    f = np.asarray(flags, dtype=bool)
+    N = f.shape[0]
+    t = np.arange(N)
+    vis = np.zeros((2 * N, 2 * N), dtype=bool)
+    vis[:N, :N] = t[None, :] <= t[:, None]                        # memory: causal
+    blk = t // block
+    vis[N:, :N] = t[None, :] < (blk * block)[:, None]            # earlier blocks' clean tokens
+    same = blk[:, None] == blk[None, :]
+    le = t[None, :] <= t[:, None]
+    fs, ft = f[None, :], f[:, None]
+    vis[N:, N:] = same & ((fs & (~ft | le)) | (~ft & ~fs & le))
+    return vis
+
+
+def dual_stream_attention(qm, km, vm, qp, kp, vp, flags, block: int, dtype: str, base: float,
+                          scale: Optional[float] = None, rows=None):
+    """Dual-Stream Masking attention of S sequences (the training-time mask
+    as a forward pass).  q*/k*/v* [S, N, H, D] float64 values before RoPE,
+    memory (m) and prediction (p) streams in logical order; flags [S, N]
+    (1 = observed) of the prediction stream.  Both streams take RoPE at the
+    shared logical positions 0..N-1; rotated q and k are rounded to the
+    storage dtype, as a decode step stores them.  GQA: query head h reads KV
+    head h // (Hq / Hkv).  rows: optional [n, 3] of (sequence, stream 0/1,
+    token) to compute (others NaN).  Returns (out_mem, out_pred), each
+    [S, N, Hq, D]."""
+    qm, km, vm, qp, kp, vp = [np.asarray(x, np.float64) for x in (qm, km, vm, qp, kp, vp)]
+    S, N, Hq, D = qm.shape
+    Hkv = km.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    ones = np.ones((S, N), np.uint8)
+    pos = np.tile(np.arange(N, dtype=np.int32), (S, 1))
+    _, qmr, kmr, _ = reorder(ones, pos, qm, km, vm, dtype, base)     # RoPE + storage rounding
+    _, qpr, kpr, _ = reorder(ones, pos, qp, kp, vp, dtype, base)
+    out = np.full((2, S, N, Hq, D), np.nan)
+    if rows is None:
+        todo = [(s, st, t) for s in range(S) for st in range(2) for t in range(N)]
+    else:
+        todo = [tuple(int(x) for x in r) for r in np.asarray(rows).reshape(-1, 3)]
+    vis_cache = {}
+    for s, st, t in todo:
+        if s not in vis_cache:
+            vis_cache[s] = dual_stream_visible(np.asarray(flags)[s], block)
+        vis = vis_cache[s][st * N + t]
+        K = np.concatenate([kmr[s], kpr[s]], axis=0)[vis]             # [nk, Hkv, D]
+        Vv = np.concatenate([vm[s], vp[s]], axis=0)[vis]
+        q = (qmr if st == 0 else qpr)[s, t]                           # [Hq, D]
+        for h in range(Hq):
+            sc = K[:, h // G, :] @ q[h] * scale
+            w = np.exp(sc - sc.max())
+            out[st, s, t, h] = (w / w.sum()) @ Vv[:, h // G, :]
+    return out[0], out[1]
+
+
 def decode_step_attention(inp, scale: Optional[float] = None, rows=None):
     """Oracle for reorder + attention on one batch drawn by
     workloads.make_attn_inputs.  Returns a dict
