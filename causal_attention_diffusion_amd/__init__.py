@@ -24,6 +24,8 @@ from .binding import (  # noqa: F401
     make_shape,
     select_workspace_tensor,
     attn_workspace_tensor,
+    dual_stream_workspace_tensor,
+    wedlm_dual_stream_attn,
     wedlm_attn_plan,
     wedlm_last_error,
     wedlm_lmhead_select_commit,

@@ -59,6 +59,10 @@ def load_library():
     lib.wedlm_lmhead_select_commit.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
                                                C.c_float, C.c_float, i32, P, sz, P]
     lib.wedlm_lmhead_select_commit.restype = C.c_int
+    lib.wedlm_dual_stream_attn_workspace.argtypes = [S, i32]
+    lib.wedlm_dual_stream_attn_workspace.restype = sz
+    lib.wedlm_dual_stream_attn.argtypes = [S, i32, P, P, P, P, P, P, P, P, P, C.c_double, P, sz, P, P]
+    lib.wedlm_dual_stream_attn.restype = C.c_int
     lib.wedlm_attn_plan.argtypes = [S, i32, C.POINTER(i32), C.POINTER(i32)]
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
@@ -276,6 +280,48 @@ def wedlm_lmhead_select_commit(hidden, lm_head, tok, filled, pos, ctx_len, n_com
         B, W, V, Dm, _ptr(hidden), _ptr(lm_head), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len),
         _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), float(alpha), float(tau),
         int(mask_id), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _dual_shape(qm, km, block):
+    import torch
+    if qm.dim() != 4 or km.dim() != 4:
+        raise WedlmError("streams must be [B, N, H, D] tensors")
+    B, N, Hq, D = qm.shape
+    Hkv = km.shape[2]
+    dt = WEDLM_BF16 if qm.dtype == torch.bfloat16 else WEDLM_F32
+    return make_shape(B, block, Hq, Hkv, D, 1, 1, dt), N
+
+
+def dual_stream_workspace_tensor(qm, km, block: int):
+    """Workspace for wedlm_dual_stream_attn (no initialisation needed)."""
+    import torch
+    shp, N = _dual_shape(qm, km, block)
+    n = int(load_library().wedlm_dual_stream_attn_workspace(C.byref(shp), int(N)))
+    if n == 0:
+        raise WedlmError(wedlm_last_error() or "unsupported dual-stream shape")
+    return torch.empty(n, dtype=torch.uint8, device=qm.device)
+
+
+def wedlm_dual_stream_attn(qm, km, vm, qp, kp, vp, flags, out_m, out_p, block: int, rope_base: float,
+                           workspace, dev_status=None, stream=None):
+    """Memory stream qm/km/vm and prediction stream qp/kp/vp [B, N, H, D]
+    (bfloat16 or float32), flags [B, N] uint8; outputs [B, N, Hq, D]."""
+    import torch
+    shp, N = _dual_shape(qm, km, block)
+    B, _, Hq, D = qm.shape
+    Hkv = km.shape[2]
+    for t, name, h in ((qm, "qm", Hq), (qp, "qp", Hq), (km, "km", Hkv), (kp, "kp", Hkv), (vm, "vm", Hkv),
+                       (vp, "vp", Hkv), (out_m, "out_m", Hq), (out_p, "out_p", Hq)):
+        _expect(t, name, (B, N, h, D), qm.dtype)
+    _expect(flags, "flags", (B, N), torch.uint8)
+    _opt(dev_status, "dev_status", (1,), torch.int32)
+    if workspace is None or workspace.dtype != torch.uint8:
+        raise WedlmError("workspace must be a uint8 tensor (dual_stream_workspace_tensor)")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load_library().wedlm_dual_stream_attn(
+        C.byref(shp), int(N), _ptr(qm), _ptr(km), _ptr(vm), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(flags),
+        _ptr(out_m), _ptr(out_p), float(rope_base), _ptr(workspace), ws_bytes, _ptr(dev_status),
+        _stream(stream)))
 
 
 def wedlm_last_error() -> str:

@@ -90,7 +90,7 @@ static int device_cus() {
     }
     return cache[dev];
 }
-static const int64_t kMaxContext = 524288;  // keys incl. the window (at most 64 splits of 8192)
+static const int64_t kMaxContext = 524288;  // keys incl. the window (at most 64 splits)
 
 struct Plan {
     int nw, chunk, RT, row_tiles, nsplit, split_keys;
@@ -139,6 +139,96 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
         p.ws_bytes = o_bytes + (rows * sizeof(float2) + 255) / 256 * 256;
     }
     return p;
+}
+
+// ---------------------------------------------------------------- Dual-Stream Masking attention
+struct DualLayout {
+    wedlm_shape sm, sp;   // memory windows (W = 64), prediction windows (W = b)
+    size_t kc, vc, qphys, perm, filled_m, pos_m, ctx_m, bt_m, pos_p, ctx_p, bt_p, attn, attn_bytes, total;
+};
+
+static int dual_layout(const wedlm_shape* s, int32_t N, DualLayout* L) {
+    if (!s) return fail(WEDLM_ERR_ARG, "shape is NULL");
+    const int b = s->W;
+    if (b != 16 && b != 32 && b != 64)
+        return fail(WEDLM_ERR_SHAPE, "dual stream: block size (shape W) must be 16, 32 or 64, got %d", b);
+    if (N < 64 || N % 64 != 0 || N > kMaxContext)
+        return fail(WEDLM_ERR_SHAPE, "dual stream: N must be a multiple of 64 in [64, %lld], got %d",
+                    (long long)kMaxContext, N);
+    if (s->B < 1 || (int64_t)s->B * N > (1ll << 24))
+        return fail(WEDLM_ERR_SHAPE, "dual stream: need 1 <= sequences and sequences*N <= 2^24");
+    const int64_t S = s->B, np = N / kPage, pool = 2 * S * np;
+    if (pool > INT32_MAX / 2) return fail(WEDLM_ERR_SHAPE, "dual stream: too many pages");
+    L->sm = *s;
+    L->sm.B = (int32_t)(S * N / 64); L->sm.W = 64;
+    L->sm.max_pages = (int32_t)np; L->sm.num_pages = (int32_t)pool; L->sm.page_size = kPage;
+    L->sp = L->sm;
+    L->sp.B = (int32_t)(S * N / b); L->sp.W = b;
+    int rc = check_shape(&L->sm);
+    if (rc) return rc;
+    rc = check_shape(&L->sp);
+    if (rc) return rc;
+    const size_t elt = s->dtype == WEDLM_F32 ? 4 : 2;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t r = o; o += up(bytes); return r; };
+    L->kc = take((size_t)pool * s->Hkv * kPage * s->D * elt);
+    L->vc = take((size_t)pool * s->Hkv * kPage * s->D * elt);
+    L->qphys = take((size_t)S * N * s->Hq * s->D * elt);
+    L->perm = take((size_t)S * N * 4);
+    L->filled_m = take((size_t)S * N);
+    L->pos_m = take((size_t)S * N * 4);
+    L->ctx_m = take((size_t)L->sm.B * 4);
+    L->bt_m = take((size_t)L->sm.B * np * 4);
+    L->pos_p = take((size_t)S * N * 4);
+    L->ctx_p = take((size_t)L->sp.B * 4);
+    L->bt_p = take((size_t)L->sp.B * np * 4);
+    const size_t wa = make_plan(&L->sm, N - 64).ws_bytes, wb = make_plan(&L->sp, N - b).ws_bytes;
+    L->attn_bytes = wa > wb ? wa : wb;
+    L->attn = take(L->attn_bytes);
+    L->total = o;
+    return WEDLM_OK;
+}
+
+extern "C" size_t wedlm_dual_stream_attn_workspace(const wedlm_shape* s, int32_t N) {
+    DualLayout L;
+    return dual_layout(s, N, &L) == WEDLM_OK ? L.total : 0;
+}
+
+extern "C" int wedlm_dual_stream_attn(const wedlm_shape* s, int32_t N, const void* qm, const void* km, const void* vm,
+                                      const void* qp, const void* kp, const void* vp, const uint8_t* flags,
+                                      void* out_m, void* out_p, double rope_base, void* workspace, size_t ws_bytes,
+                                      int32_t* dev_status, void* stream) {
+    DualLayout L;
+    int rc = dual_layout(s, N, &L);
+    if (rc) return rc;
+    if (!qm || !km || !vm || !qp || !kp || !vp || !flags || !out_m || !out_p)
+        return fail(WEDLM_ERR_ARG, "wedlm_dual_stream_attn: NULL device pointer");
+    if (!workspace || ws_bytes < L.total)
+        return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace ? ws_bytes : 0);
+    char* ws = static_cast<char*>(workspace);
+    auto I32 = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
+    hipStream_t st = (hipStream_t)stream;
+    rc = hip_status(launch_dual_layout(reinterpret_cast<uint8_t*>(ws + L.filled_m), I32(L.pos_m), I32(L.ctx_m),
+                                       I32(L.bt_m), I32(L.pos_p), I32(L.ctx_p), I32(L.bt_p), s->B, N, s->W, st),
+                    "wedlm_dual_stream_attn layout");
+    if (rc) return rc;
+    void* kc = ws + L.kc;
+    void* vc = ws + L.vc;
+    void* qph = ws + L.qphys;
+    // memory stream: all-observed 64-token windows over the sequence's memory pages
+    rc = wedlm_reorder(&L.sm, reinterpret_cast<uint8_t*>(ws + L.filled_m), I32(L.pos_m), qm, km, vm, qph, kc, vc,
+                       I32(L.bt_m), I32(L.ctx_m), I32(L.perm), rope_base, dev_status, stream);
+    if (rc) return rc;
+    rc = wedlm_step_attn(&L.sm, qph, kc, vc, I32(L.bt_m), I32(L.ctx_m), I32(L.perm), out_m, 0.f, N - 64,
+                         ws + L.attn, L.attn_bytes, dev_status, stream);
+    if (rc) return rc;
+    // prediction stream: block windows over the memory prefix and their own pages
+    rc = wedlm_reorder(&L.sp, flags, I32(L.pos_p), qp, kp, vp, qph, kc, vc, I32(L.bt_p), I32(L.ctx_p), I32(L.perm),
+                       rope_base, dev_status, stream);
+    if (rc) return rc;
+    return wedlm_step_attn(&L.sp, qph, kc, vc, I32(L.bt_p), I32(L.ctx_p), I32(L.perm), out_p, 0.f, N - s->W,
+                           ws + L.attn, L.attn_bytes, dev_status, stream);
 }
 
 // ---------------------------------------------------------------- LM head + select / commit

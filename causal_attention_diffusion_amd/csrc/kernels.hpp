@@ -90,6 +90,8 @@ hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t 
 int attn_chunk(int dtype, int nw);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
+hipError_t launch_dual_layout(uint8_t* filled_m, int32_t* pos_m, int32_t* ctx_m, int32_t* bt_m, int32_t* pos_p,
+                              int32_t* ctx_p, int32_t* bt_p, int S, int N, int b, hipStream_t stream);
 // commit / Eq. 11 select / refill alone, on row partials already in a.part
 hipError_t launch_commit(const SelectArgs& a, hipStream_t stream);
 

@@ -242,6 +242,51 @@ int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32_t Dm, cons
                                int32_t mask_id, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * wedlm_dual_stream_attn_workspace -- bytes of device workspace for
+ * wedlm_dual_stream_attn (the paged K/V cache of both streams, rotated
+ * queries, block tables and the attention partials); 0 if the shape is not
+ * supported.
+ */
+size_t wedlm_dual_stream_attn_workspace(const wedlm_shape *s, int32_t N);
+
+/*
+ * wedlm_dual_stream_attn -- Dual-Stream Masking attention, forward.
+ * (paper-summary page, "Method", training paragraph, and "Key claims",
+ * sec. 4.2, Eq. 8-10: a clean memory stream and a block-masked prediction
+ * stream share position ids; prediction tokens of block i attend to the
+ * memory tokens whose logical positions precede block i.)
+ *
+ * For each of s->B sequences of N tokens at logical positions 0..N-1:
+ *   memory token t      sees memory tokens 0..t (causal);
+ *   prediction token t  of block i = t / b sees memory tokens 0..i*b-1 and
+ *                       the prediction tokens u of its own block with
+ *                       (u observed and (t masked or u <= t)) or
+ *                       (both masked and u <= t)
+ * (Topological Reordering under the causal mask inside the block; the
+ * memory rule inside the stream and the block rule are this library's
+ * reading of the page).  Both streams take RoPE at the logical positions
+ * as in wedlm_reorder; softmax scale 1/sqrt(D).  Computed as two
+ * (wedlm_reorder, wedlm_step_attn) pairs on one paged cache: the memory
+ * stream as all-observed 64-token windows, each prediction block as one
+ * decode-step window over the memory prefix.
+ *
+ *   s        B = sequences, W = block size b (16, 32 or 64), Hq, Hkv, D,
+ *            dtype as for wedlm_step_attn; page_size 16; max_pages and
+ *            num_pages are ignored
+ *   N        tokens per sequence, a multiple of 64
+ *   qm, km, vm  memory stream [B][N][Hq|Hkv][D] device, before RoPE
+ *   qp, kp, vp  prediction stream, same layout
+ *   flags    [B][N] uint8 device, 1 = observed, 0 = masked (prediction)
+ *   out_m, out_p  [B][N][Hq][D] device out, logical order
+ *   workspace / ws_bytes  see wedlm_dual_stream_attn_workspace
+ *   dev_status  device int32 or NULL
+ */
+int wedlm_dual_stream_attn(const wedlm_shape *s, int32_t N, const void *qm, const void *km, const void *vm,
+                           const void *qp, const void *kp, const void *vp, const uint8_t *flags,
+                           void *out_m, void *out_p, double rope_base, void *workspace, size_t ws_bytes,
+                           int32_t *dev_status, void *stream);
+
+/*
  * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for
  * this shape and bound: work-groups per (sequence, KV head, row tile)
  * (*nsplit) and keys per work-group (*split_keys).  Either may be NULL.

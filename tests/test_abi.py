@@ -206,3 +206,17 @@ def test_lmhead_validation_and_workspace():
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, *small) == ERR_WS
     nan = args[:10] + [C.c_float(float("nan"))] + args[11:]
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, *nan) == ERR_ARG
+
+
+def test_dual_stream_validation():
+    lib = wd.load_library()
+    ok = wd.make_shape(1, 32, 4, 2, 64, 1, 1, wd.WEDLM_BF16)
+    assert lib.wedlm_dual_stream_attn_workspace(C.byref(ok), 256) > 0
+    for W, N in [(8, 256), (48, 256), (32, 100), (32, 0)]:
+        bad = wd.make_shape(1, W, 4, 2, 64, 1, 1, wd.WEDLM_BF16)
+        assert lib.wedlm_dual_stream_attn_workspace(C.byref(bad), N) == 0, (W, N)
+    fake = C.c_void_p(0x1000)
+    assert lib.wedlm_dual_stream_attn(C.byref(ok), 256, *([fake] * 8), None, 1e6, fake, 1 << 40, None,
+                                      None) == ERR_ARG
+    need = lib.wedlm_dual_stream_attn_workspace(C.byref(ok), 256)
+    assert lib.wedlm_dual_stream_attn(C.byref(ok), 256, *([fake] * 9), 1e6, fake, need - 1, None, None) == ERR_WS
