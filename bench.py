@@ -53,10 +53,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_b4",
                     choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32", "select_v152k",
-                             "lmhead_v152k"],
+                             "lmhead_v152k", "dualstream_n4096"],
                     help="select_v152k times the select/commit call alone (batch 64 x window 16, "
                          "V=151936, streaming from an all-masked window); lmhead_v152k the fused "
-                         "LM head + select call (hidden 4096) on the same window")
+                         "LM head + select call (hidden 4096) on the same window; dualstream_n4096 the "
+                         "Dual-Stream Masking attention over 4 x 4096 tokens, blocks of 32")
     ap.add_argument("--vocab", type=int, default=151936)
     ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
@@ -104,6 +105,9 @@ def main():
         return
     if args.workload == "lmhead_v152k":
         bench_lmhead(args)
+        return
+    if args.workload == "dualstream_n4096":
+        bench_dual(args)
         return
 
     import torch
@@ -516,6 +520,105 @@ def bench_lmhead(args):
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_lmhead(cfg, args, w, hidden[0])
     print(json.dumps(result), flush=True)
+
+
+def bench_dual(args):
+    """Dual-Stream Masking attention forward: 4 sequences of 4096 tokens,
+    blocks of 32, 32 query / 8 KV heads of 128, bf16, RoPE base 1e6.  Both
+    streams N(0,1); each block's observed fraction is drawn uniformly in
+    [0.2, 0.8] and its observed tokens at random.  A step is one call (both
+    streams of all sequences)."""
+    import torch
+    import causal_attention_diffusion_amd as wd
+
+    dev = torch.device("cuda:0")
+    S, N, b, Hq, Hkv, D = 4, 4096, 32, 32, 8, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(1401)
+
+    def draw(h):
+        return torch.randn((S, N, h, D), generator=g, device=dev).to(torch.bfloat16)
+
+    qm, km, vm, qp, kp, vp = draw(Hq), draw(Hkv), draw(Hkv), draw(Hq), draw(Hkv), draw(Hkv)
+    frac = torch.rand((S, N // b, 1), generator=g, device=dev) * 0.6 + 0.2
+    flags = (torch.rand((S, N // b, b), generator=g, device=dev) < frac).reshape(S, N).to(torch.uint8)
+    out_m, out_p = torch.empty_like(qm), torch.empty_like(qp)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = wd.dual_stream_workspace_tensor(qm, km, b)
+
+    def step():
+        wd.wedlm_dual_stream_attn(qm, km, vm, qp, kp, vp, flags, out_m, out_p, b, 1e6, ws, dev_status=status)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = ev0.elapsed_time(ev1) / args.steps
+    if status.item() != 0:
+        print(f"device status {status.item()}", file=sys.stderr)
+        sys.exit(3)
+    # algorithmic bytes: every window reads K and V of its visible keys once
+    # (memory: 64-token windows c see 64(c+1) keys; prediction: block i sees
+    # b(i+1)), plus q, k, v of both streams in and both outputs out
+    nm, nb = N // 64, N // b
+    keys = S * (64 * nm * (nm + 1) // 2 + b * nb * (nb + 1) // 2)
+    alg_bytes = float(keys) * Hkv * D * 2 * 2 + 2.0 * S * N * (2 * Hq + 2 * Hkv) * D * 2
+    # flops: 4 D per (query head, visible key) -- memory token t sees t+1
+    # keys; a prediction token sees its block start plus its block part
+    pairs_m = N * (N + 1) // 2
+    pairs_p = sum(i * b * b for i in range(nb)) + nb * b * (b + 1) // 2   # upper bound inside blocks
+    flops = 4.0 * D * Hq * S * (pairs_m + pairs_p)
+    gbs = alg_bytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(2 * S * N / (call_ms * 1e-3), 1),
+        "unit": "tokens/s (both streams)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(call_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "graph": False, "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "config": {"workload": f"dualstream_n4096: {S} sequences x {N} tokens, blocks of {b}, Hq={Hq} Hkv={Hkv} "
+                               f"D={D} bf16, memory + prediction stream attention",
+                   "sequences": S, "tokens": N, "block": b},
+        "dual_stream": {"avg_ms": round(call_ms, 5), "alg_bytes_per_launch": int(alg_bytes),
+                        "GB_per_s": round(gbs, 1), "alg_flops_upper": int(flops),
+                        "TFLOP_per_s_upper": round(flops / (call_ms * 1e-3) / 1e12, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "wedlm_dual_stream_attn (layout + 2 x (reorder + attn_split + combine))"},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_dual(args, [x[:1].float().cpu().numpy().astype(np.float64)
+                                                          for x in (qm, km, vm, qp, kp, vp)],
+                                                   flags[:1].cpu().numpy(), b)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_dual(args, arrs, flags, b):
+    """The oracle on sampled tokens of the first sequence (both streams),
+    scaled to tokens/s."""
+    import oracle
+    N = arrs[0].shape[1]
+    rng = np.random.default_rng(5)
+    reps, dt_s, n = 0, 0.0, 0
+    while reps < 64 and dt_s < 10.0:
+        toks = rng.integers(0, N, 16)
+        rows = np.array([(0, st, t) for st in (0, 1) for t in toks])
+        t0 = time.perf_counter()
+        oracle.dual_stream_attention(*arrs, flags, b, "bf16", 1e6, rows=rows)
+        dt_s += time.perf_counter() - t0
+        n += len(rows)
+        reps += 1
+    return {"value": round(n / dt_s, 2), "unit": "tokens/s (both streams)", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{n} uniformly drawn tokens of one 4096-token sequence (both "
+                                        f"streams, all 32 heads); {dt_s:.2f} s"}
 
 
 def cpu_baseline_lmhead(cfg, args, w_dev, h_dev):
