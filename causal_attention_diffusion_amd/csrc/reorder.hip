@@ -52,36 +52,35 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
 
     // Work items are 4 consecutive pairs (c .. c+3 with c+D/2 .. c+D/2+3) of
     // one head: Hq query heads, then Hkv key heads; value rows are copied in
-    // 4-element pieces.  The rows of slot i depend on nothing else, so the
-    // first batch of loads is issued before the permutation, the page and the
-    // angle table are known.
-    constexpr int kMaxItems = 4;
+    // 4-element pieces.
     const int qn = a.Hq * (half / 4), kn = a.Hkv * (half / 4), vn = a.Hkv * (D / 4);
     const int n_all = qn + kn + vn;
     const T* qs = static_cast<const T*>(a.q) + ((size_t)b * W + i) * a.Hq * D;
     const T* ks = static_cast<const T*>(a.k) + ((size_t)b * W + i) * a.Hkv * D;
     const T* vs = static_cast<const T*>(a.v) + ((size_t)b * W + i) * a.Hkv * D;
-    float x0[kMaxItems][4], x1[kMaxItems][4];
-    auto load_items = [&](int base) {
-#pragma unroll
-        for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * 256;
-            if (it >= n_all) continue;
-            if (it < qn + kn) {
-                const bool isq = it < qn;
-                const int j = isq ? it : it - qn;
-                const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-                const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
-                load4(src, x0[u]);
-                load4(src + half, x1[u]);
-            } else {
-                const int j = it - qn - kn;
-                load4(vs + (size_t)j * 4, x0[u]);
-            }
-        }
-    };
 
-    load_items(tid);
+    // The rows of slot i depend on nothing else, so the first batch of
+    // kMaxItems items per thread is loaded before the permutation, the page
+    // and the angle table are known.  (Plain code, no lambdas: arrays
+    // captured by a lambda were kept in scratch memory by the compiler.)
+    constexpr int kMaxItems = 4;
+    float x0[kMaxItems][4], x1[kMaxItems][4];
+#pragma unroll
+    for (int u = 0; u < kMaxItems; ++u) {
+        const int it = tid + u * 256;
+        if (it >= n_all) continue;
+        if (it < qn + kn) {
+            const bool isq = it < qn;
+            const int j = isq ? it : it - qn;
+            const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
+            const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
+            load4(src, x0[u]);
+            load4(src + half, x1[u]);
+        } else {
+            const int j = it - qn - kn;
+            load4(vs + (size_t)j * 4, x0[u]);
+        }
+    }
 
     // Every wave derives the physical row of slot i by itself from two
     // ballots and a prefix popcount: no LDS, no barrier.
@@ -95,6 +94,15 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
     const int n_obs = __popcll(fm);
     const int r = ((fm >> i) & 1ull) ? __popcll(fm & below) : n_obs + __popcll(mm & below);
     const int p = __shfl(p_lane, i);
+
+    // cos/sin of the D/2 pair angles, float64, once per work-group
+    __shared__ double s_cs[64], s_sn[64];
+    if (tid < half) {
+        double sn, cs;
+        sincos((double)p * exp2(-(2.0 * tid / D) * a.log2_base), &sn, &cs);
+        s_cs[tid] = cs;
+        s_sn[tid] = sn;
+    }
 
     // The window's tokens L .. L+W-1 span at most W/16 + 2 pages: their
     // block-table entries are read as soon as L is known, one per lane.
@@ -124,10 +132,27 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
     T* qd = static_cast<T*>(a.q_phys) + ((size_t)b * W + r) * a.Hq * D;
     T* kc = static_cast<T*>(a.k_cache);
     T* vc = static_cast<T*>(a.v_cache);
+    __syncthreads();
 
-    // cos/sin of the D/2 pair angles, float64, once per work-group
-    __shared__ double s_cs[64], s_sn[64];
-    auto store_items = [&](int base) {
+    // Every later batch loads all its items before using any.
+    for (int base = tid; base < n_all; base += kMaxItems * 256) {
+        if (base != tid)   // the first batch is already loaded
+#pragma unroll
+        for (int u = 0; u < kMaxItems; ++u) {
+            const int it = base + u * 256;
+            if (it >= n_all) continue;
+            if (it < qn + kn) {
+                const bool isq = it < qn;
+                const int j = isq ? it : it - qn;
+                const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
+                const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
+                load4(src, x0[u]);
+                load4(src + half, x1[u]);
+            } else {
+                const int j = it - qn - kn;
+                load4(vs + (size_t)j * 4, x0[u]);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
             const int it = base + u * 256;
@@ -152,19 +177,6 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
                 store4(vc + (row0 + (size_t)g * kPage) * D + d, x0[u]);
             }
         }
-    };
-
-    if (tid < half) {
-        double sn, cs;
-        sincos((double)p * exp2(-(2.0 * tid / D) * a.log2_base), &sn, &cs);
-        s_cs[tid] = cs;
-        s_sn[tid] = sn;
-    }
-    __syncthreads();
-    store_items(tid);
-    for (int base = tid + kMaxItems * 256; base < n_all; base += kMaxItems * 256) {
-        load_items(base);
-        store_items(base);
     }
 }
 

@@ -1,5 +1,5 @@
-"""Register budget of the attention kernels (host-only: compiles the HIP
-source to gfx950 assembly and reads the kernel metadata).
+"""Register and scratch budget of the kernels (host-only: compiles the HIP
+sources to gfx950 assembly and reads the kernel metadata).
 
 Every attention kernel must fit its registers without spilling to scratch:
 a spill puts scratch traffic inside the key loop (it cost the 64-row
@@ -31,7 +31,8 @@ def _kernel_meta(src):
         if not name:
             continue
         vals = {k: int(v) for k, v in re.findall(r"\.(vgpr_count|vgpr_spill_count|sgpr_spill_count|"
-                                                 r"agpr_count|group_segment_fixed_size):\s+(\d+)", block)}
+                                                 r"agpr_count|group_segment_fixed_size|"
+                                                 r"private_segment_fixed_size):\s+(\d+)", block)}
         meta[name.group(1)] = vals
     return meta
 
@@ -47,3 +48,14 @@ def test_attention_kernels_do_not_spill(src):
         assert v.get("sgpr_spill_count", 0) == 0, (name, v)
         budget = 256 if "bf16" in name else 512
         assert v.get("vgpr_count", 0) + v.get("agpr_count", 0) <= budget, (name, v)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+@pytest.mark.parametrize("src", sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")))
+def test_no_kernel_uses_scratch(src):
+    meta = _kernel_meta(src)
+    if not meta:
+        pytest.skip(f"{src} holds host code only")
+    for name, v in meta.items():
+        assert "private_segment_fixed_size" in v, name
+        assert v["private_segment_fixed_size"] == 0, (name, v)
