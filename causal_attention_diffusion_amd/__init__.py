@@ -19,7 +19,9 @@ from .binding import (  # noqa: F401
     WedlmError,
     attn_plan,
     lib_path,
+    ModelHandle,
     lmhead_workspace_tensor,
+    model_step_workspace_tensor,
     load_library,
     make_shape,
     select_workspace_tensor,
@@ -29,6 +31,7 @@ from .binding import (  # noqa: F401
     wedlm_attn_plan,
     wedlm_last_error,
     wedlm_lmhead_select_commit,
+    wedlm_model_step,
     wedlm_lmhead_select_commit_workspace,
     wedlm_reorder,
     wedlm_select_commit,

@@ -28,6 +28,19 @@ class WedlmShape(C.Structure):
                 ("num_pages", C.c_int32), ("dtype", C.c_int32)]
 
 
+LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down", "k_cache", "v_cache")
+
+
+class WedlmLayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in LAYER_FIELDS]
+
+
+class WedlmModel(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("d_ff", C.c_int32), ("vocab", C.c_int32),
+                ("rms_eps", C.c_float), ("embed", C.c_void_p), ("final_norm", C.c_void_p),
+                ("lm_head", C.c_void_p), ("layers", C.POINTER(WedlmLayerWeights))]
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -63,6 +76,12 @@ def load_library():
     lib.wedlm_dual_stream_attn_workspace.restype = sz
     lib.wedlm_dual_stream_attn.argtypes = [S, i32, P, P, P, P, P, P, P, P, P, C.c_double, P, sz, P, P]
     lib.wedlm_dual_stream_attn.restype = C.c_int
+    Mp = C.POINTER(WedlmModel)
+    lib.wedlm_model_step_workspace.argtypes = [Mp, S, i32]
+    lib.wedlm_model_step_workspace.restype = sz
+    lib.wedlm_model_step.argtypes = [Mp, S, P, P, P, P, P, P, P, P, P, P, C.c_float, C.c_float, C.c_double, i32,
+                                     P, sz, P, P]
+    lib.wedlm_model_step.restype = C.c_int
     lib.wedlm_attn_plan.argtypes = [S, i32, C.POINTER(i32), C.POINTER(i32)]
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
@@ -322,6 +341,67 @@ def wedlm_dual_stream_attn(qm, km, vm, qp, kp, vp, flags, out_m, out_p, block: i
         C.byref(shp), int(N), _ptr(qm), _ptr(km), _ptr(vm), _ptr(qp), _ptr(kp), _ptr(vp), _ptr(flags),
         _ptr(out_m), _ptr(out_p), float(rope_base), _ptr(workspace), ws_bytes, _ptr(dev_status),
         _stream(stream)))
+
+
+class ModelHandle:
+    """The C description of a synthetic decoder whose weights and per-layer
+    caches are torch tensors (kept alive here).  weights: dict with embed
+    [vocab+1, d], final_norm [d], lm_head [vocab, d] and layers: list of
+    dicts with the LAYER_FIELDS entries (bfloat16 tensors on the GPU)."""
+
+    def __init__(self, weights, rms_eps: float = 1e-6):
+        import torch
+        self.weights = weights
+        layers = weights["layers"]
+        self.layer_array = (WedlmLayerWeights * len(layers))()
+        for i, lw in enumerate(layers):
+            for n in LAYER_FIELDS:
+                t = lw[n]
+                if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device.type != "cuda":
+                    raise WedlmError(f"layer {i} {n}: expected a contiguous bfloat16 GPU tensor")
+                setattr(self.layer_array[i], n, t.data_ptr())
+        d = weights["final_norm"].shape[0]
+        vocab = weights["lm_head"].shape[0]
+        if tuple(weights["embed"].shape) != (vocab + 1, d):
+            raise WedlmError("embed must be [vocab + 1, d_model]")
+        self.model = WedlmModel(len(layers), d, layers[0]["w_gate"].shape[0], vocab, float(rms_eps),
+                                _ptr(weights["embed"]), _ptr(weights["final_norm"]), _ptr(weights["lm_head"]),
+                                C.cast(self.layer_array, C.POINTER(WedlmLayerWeights)))
+        self.vocab = vocab
+        self.d_model = d
+
+
+def model_step_workspace_tensor(handle: ModelHandle, shape: WedlmShape, max_ctx_len: int, device):
+    import torch
+    n = int(load_library().wedlm_model_step_workspace(C.byref(handle.model), C.byref(shape), int(max_ctx_len)))
+    if n == 0:
+        raise WedlmError(wedlm_last_error() or "unsupported model shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def wedlm_model_step(handle: ModelHandle, shape: WedlmShape, block_table, tok, filled, pos, ctx_len, n_commit,
+                     committed, alpha: float, tau: float, rope_base: float, max_ctx_len: int, workspace,
+                     argmax_out=None, entropy_out=None, hidden_out=None, dev_status=None, stream=None):
+    import torch
+    B, W = shape.B, shape.W
+    _expect(block_table, "block_table", (B, shape.max_pages), torch.int32)
+    _expect(tok, "tok", (B, W), torch.int32)
+    _expect(filled, "filled", (B, W), torch.uint8)
+    _expect(pos, "pos", (B, W), torch.int32)
+    _expect(ctx_len, "ctx_len", (B,), torch.int32)
+    _expect(n_commit, "n_commit", (B,), torch.int32)
+    _expect(committed, "committed", (B, W), torch.int32)
+    _opt(argmax_out, "argmax_out", (B, W), torch.int32)
+    _opt(entropy_out, "entropy_out", (B, W), torch.float32)
+    _opt(hidden_out, "hidden_out", (B, W, handle.d_model), torch.bfloat16)
+    _opt(dev_status, "dev_status", (1,), torch.int32)
+    if workspace is None or workspace.dtype != torch.uint8:
+        raise WedlmError("workspace must be a uint8 tensor (model_step_workspace_tensor)")
+    _check(load_library().wedlm_model_step(
+        C.byref(handle.model), C.byref(shape), _ptr(block_table), _ptr(tok), _ptr(filled), _ptr(pos),
+        _ptr(ctx_len), _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(hidden_out),
+        float(alpha), float(tau), float(rope_base), int(max_ctx_len), _ptr(workspace),
+        workspace.numel(), _ptr(dev_status), _stream(stream)))
 
 
 def wedlm_last_error() -> str:

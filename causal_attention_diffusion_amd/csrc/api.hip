@@ -297,6 +297,154 @@ extern "C" int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32
     return hip_status(launch_commit(a, st), "wedlm_lmhead_select_commit launch");
 }
 
+// ---------------------------------------------------------------- synthetic decoder step
+struct ModelLayout {
+    size_t x_res, h, q, k, v, qphys, perm, o, act, P1, P2, attn, lm, total;
+    size_t attn_bytes, lm_bytes;
+    int Sq, Skv, So, Sgu, Sd;
+};
+
+static int model_layout(const wedlm_model* m, const wedlm_shape* s, int32_t max_ctx_len, ModelLayout* L) {
+    if (!m || !s) return fail(WEDLM_ERR_ARG, "model or shape is NULL");
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->dtype != WEDLM_BF16) return fail(WEDLM_ERR_UNSUPPORTED, "wedlm_model_step runs in bf16");
+    if (m->n_layers < 1 || !m->layers || !m->embed || !m->final_norm || !m->lm_head)
+        return fail(WEDLM_ERR_ARG, "model: need n_layers >= 1 and embed, final_norm, lm_head, layers");
+    if (m->d_model != s->Hq * s->D || m->d_model % 256 || m->d_ff < 256 || m->d_ff % 256 || m->vocab < 1)
+        return fail(WEDLM_ERR_SHAPE, "model: need d_model = Hq*D, d_model and d_ff multiples of 256, vocab >= 1");
+    if (!(m->rms_eps > 0.f) || !isfinite(m->rms_eps)) return fail(WEDLM_ERR_ARG, "model: rms_eps must be > 0");
+    const int64_t M = (int64_t)s->B * s->W;
+    if (M > 4096) return fail(WEDLM_ERR_SHAPE, "model: B*W must be <= 4096");
+    if (max_ctx_len < 0 || (int64_t)max_ctx_len + s->W > kMaxContext)
+        return fail(WEDLM_ERR_UNSUPPORTED, "context beyond %lld tokens", (long long)kMaxContext);
+    LmheadLayout LL;
+    if (!lmhead_layout(s->B, s->W, m->vocab, m->d_model, &LL))
+        return fail(WEDLM_ERR_SHAPE, "model: LM head shape not supported");
+    const int d = m->d_model, F = m->d_ff, HqD = s->Hq * s->D, HkvD = s->Hkv * s->D;
+    L->Sq = gemm_splits((int)M, HqD, d);
+    L->Skv = gemm_splits((int)M, HkvD, d);
+    L->So = gemm_splits((int)M, d, HqD);
+    L->Sgu = gemm_splits((int)M, F, d);
+    L->Sd = gemm_splits((int)M, d, F);
+    size_t pmax = 0;
+    for (size_t x : {(size_t)L->Sq * HqD, (size_t)L->Skv * HkvD, (size_t)L->So * d, (size_t)L->Sgu * F,
+                     (size_t)L->Sd * d})
+        pmax = x > pmax ? x : pmax;
+    pmax *= (size_t)M * 4;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t r = o; o += up(bytes); return r; };
+    L->x_res = take((size_t)M * d * 4);
+    L->h = take((size_t)M * d * 2);
+    L->q = take((size_t)M * HqD * 2);
+    L->k = take((size_t)M * HkvD * 2);
+    L->v = take((size_t)M * HkvD * 2);
+    L->qphys = take((size_t)M * HqD * 2);
+    L->perm = take((size_t)M * 4);
+    L->o = take((size_t)M * HqD * 2);
+    L->act = take((size_t)M * F * 2);
+    L->P1 = take(pmax);
+    L->P2 = take(pmax);
+    L->attn_bytes = make_plan(s, max_ctx_len).ws_bytes;
+    L->attn = take(L->attn_bytes);
+    L->lm_bytes = LL.total;
+    L->lm = take(L->lm_bytes);
+    L->total = o;
+    return WEDLM_OK;
+}
+
+extern "C" size_t wedlm_model_step_workspace(const wedlm_model* m, const wedlm_shape* s, int32_t max_ctx_len) {
+    ModelLayout L;
+    return model_layout(m, s, max_ctx_len, &L) == WEDLM_OK ? L.total : 0;
+}
+
+extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, const int32_t* block_table, int32_t* tok,
+                                uint8_t* filled, int32_t* pos, int32_t* ctx_len, int32_t* n_commit, int32_t* committed,
+                                int32_t* argmax_out, float* entropy_out, void* hidden_out, float alpha, float tau,
+                                double rope_base, int32_t max_ctx_len, void* workspace, size_t ws_bytes,
+                                int32_t* dev_status, void* stream) {
+    ModelLayout L;
+    int rc = model_layout(m, s, max_ctx_len, &L);
+    if (rc) return rc;
+    if (!block_table || !tok || !filled || !pos || !ctx_len || !n_commit || !committed)
+        return fail(WEDLM_ERR_ARG, "wedlm_model_step: NULL device pointer");
+    for (int l = 0; l < m->n_layers; ++l) {
+        const wedlm_layer_weights& w = m->layers[l];
+        if (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.wo || !w.mlp_norm || !w.w_gate || !w.w_up || !w.w_down ||
+            !w.k_cache || !w.v_cache)
+            return fail(WEDLM_ERR_ARG, "wedlm_model_step: layer %d has a NULL pointer", l);
+    }
+    if (!workspace || ws_bytes < L.total)
+        return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace ? ws_bytes : 0);
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t st = (hipStream_t)stream;
+    const int M = s->B * s->W, d = m->d_model, F = m->d_ff, HqD = s->Hq * s->D, HkvD = s->Hkv * s->D;
+    auto bf = [&](size_t off) { return reinterpret_cast<bf16_t*>(ws + off); };
+    auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    auto cbf = [](const void* p) { return static_cast<const bf16_t*>(p); };
+    auto gemm = [&](const void* W, const bf16_t* X, float* P, int N, int K, int S) {
+        GemmArgs g{cbf(W), X, P, M, N, K, S, 1};
+        return hip_status(launch_gemm(g, st), "wedlm_model_step gemm");
+    };
+    auto rows = [&](const float* P, const float* Pg, bf16_t* out, int N, int S, const void* norm) {
+        ModelRowArgs r{};
+        r.x_res = f32(L.x_res); r.h = out; r.g = cbf(norm); r.P = P; r.Pg = Pg;
+        r.M = M; r.N = N; r.S = S; r.eps = m->rms_eps; r.status = dev_status;
+        return r;
+    };
+    {
+        ModelRowArgs r = rows(nullptr, nullptr, bf(L.h), d, 0, m->layers[0].attn_norm);
+        r.tok = tok; r.embed = cbf(m->embed); r.n_embed = m->vocab + 1;
+        rc = hip_status(launch_embed_rmsnorm(r, st), "wedlm_model_step embed");
+        if (rc) return rc;
+    }
+    for (int l = 0; l < m->n_layers; ++l) {
+        const wedlm_layer_weights& w = m->layers[l];
+        const void* next_norm = l + 1 < m->n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
+        // q, k, v projections of the normalised window rows
+        struct { const void* W; size_t out; int N, S; } proj[3] = {
+            {w.wq, L.q, HqD, L.Sq}, {w.wk, L.k, HkvD, L.Skv}, {w.wv, L.v, HkvD, L.Skv}};
+        for (auto& pj : proj) {
+            if ((rc = gemm(pj.W, bf(L.h), f32(L.P1), pj.N, d, pj.S))) return rc;
+            if ((rc = hip_status(launch_finish_rows(rows(f32(L.P1), nullptr, bf(pj.out), pj.N, pj.S, nullptr), st),
+                                 "wedlm_model_step finish")))
+                return rc;
+        }
+        // reorder + RoPE + append into this layer's cache, then attention
+        rc = wedlm_reorder(s, filled, pos, ws + L.q, ws + L.k, ws + L.v, ws + L.qphys, w.k_cache, w.v_cache,
+                           block_table, ctx_len, reinterpret_cast<int32_t*>(ws + L.perm), rope_base, dev_status, stream);
+        if (rc) return rc;
+        rc = wedlm_step_attn(s, ws + L.qphys, w.k_cache, w.v_cache, block_table, ctx_len,
+                             reinterpret_cast<int32_t*>(ws + L.perm), ws + L.o, 0.f, max_ctx_len, ws + L.attn,
+                             L.attn_bytes, dev_status, stream);
+        if (rc) return rc;
+        // x += o Wo^T; h = RMSNorm(x) * mlp_norm
+        if ((rc = gemm(w.wo, bf(L.o), f32(L.P1), d, HqD, L.So))) return rc;
+        if ((rc = hip_status(launch_add_rmsnorm(rows(f32(L.P1), nullptr, bf(L.h), d, L.So, w.mlp_norm), st),
+                             "wedlm_model_step norm")))
+            return rc;
+        // act = silu(h Wg^T) * (h Wu^T); x += act Wd^T; h = RMSNorm(x) * next norm
+        if ((rc = gemm(w.w_gate, bf(L.h), f32(L.P2), F, d, L.Sgu))) return rc;
+        if ((rc = gemm(w.w_up, bf(L.h), f32(L.P1), F, d, L.Sgu))) return rc;
+        if ((rc = hip_status(launch_finish_rows(rows(f32(L.P1), f32(L.P2), bf(L.act), F, L.Sgu, nullptr), st),
+                             "wedlm_model_step finish")))
+            return rc;
+        if ((rc = gemm(w.w_down, bf(L.act), f32(L.P1), d, F, L.Sd))) return rc;
+        if ((rc = hip_status(launch_add_rmsnorm(rows(f32(L.P1), nullptr, bf(L.h), d, L.Sd, next_norm), st),
+                             "wedlm_model_step norm")))
+            return rc;
+    }
+    if (hidden_out) {
+        rc = hip_status(hipMemcpyAsync(hidden_out, ws + L.h, (size_t)M * d * 2, hipMemcpyDeviceToDevice, st),
+                        "wedlm_model_step hidden copy");
+        if (rc) return rc;
+    }
+    return wedlm_lmhead_select_commit(s->B, s->W, m->vocab, d, ws + L.h, m->lm_head, tok, filled, pos, ctx_len,
+                                      n_commit, committed, argmax_out, entropy_out, alpha, tau, m->vocab, ws + L.lm,
+                                      L.lm_bytes, stream);
+}
+
 extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_t* nsplit, int32_t* split_keys) {
     int rc = check_shape(s);
     if (rc) return rc;

@@ -89,6 +89,30 @@ hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
 int attn_chunk(int dtype, int nw);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+struct ModelRowArgs {
+    const int32_t* tok;     // embed: window token ids [M]
+    const bf16_t* embed;    // embed: [n_embed][N]
+    int n_embed;
+    float* x_res;           // residual stream [M][N] fp32
+    bf16_t* h;              // bf16 output [M][N]
+    const bf16_t* g;        // RMSNorm weight [N]
+    const float* P;         // split-K partials [S][M][N]
+    const float* Pg;        // gate partials for the SwiGLU finish, or nullptr
+    int M, N, S;
+    float eps;
+    int32_t* status;
+};
+struct GemmArgs {
+    const bf16_t* W;        // [N][K]
+    const bf16_t* X;        // [M][K]
+    float* P;               // [S][M][N] partial products
+    int M, N, K, S, nrg;    // nrg set by the launcher
+};
+int gemm_splits(int M, int N, int K);
+hipError_t launch_gemm(GemmArgs a, hipStream_t stream);
+hipError_t launch_embed_rmsnorm(const ModelRowArgs& a, hipStream_t stream);
+hipError_t launch_add_rmsnorm(const ModelRowArgs& a, hipStream_t stream);
+hipError_t launch_finish_rows(const ModelRowArgs& a, hipStream_t stream);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
 hipError_t launch_dual_layout(uint8_t* filled_m, int32_t* pos_m, int32_t* ctx_m, int32_t* bt_m, int32_t* pos_p,
                               int32_t* ctx_p, int32_t* bt_p, int S, int N, int b, hipStream_t stream);

@@ -77,6 +77,7 @@ typedef enum { WEDLM_F32 = 0, WEDLM_BF16 = 1 } wedlm_dtype;
 #define WEDLM_DEV_BAD_PAGE 2u  /* a needed block_table entry is outside [0, num_pages) */
 #define WEDLM_DEV_BAD_PERM 4u  /* a permutation entry is outside [0, W) */
 #define WEDLM_DEV_BAD_POS 8u   /* positions negative or not strictly increasing */
+#define WEDLM_DEV_BAD_TOKEN 16u /* a window token id outside [0, vocab] (wedlm_model_step) */
 
 typedef struct {
     int32_t B;          /* sequences */
@@ -285,6 +286,66 @@ int wedlm_dual_stream_attn(const wedlm_shape *s, int32_t N, const void *qm, cons
                            const void *qp, const void *kp, const void *vp, const uint8_t *flags,
                            void *out_m, void *out_p, double rope_base, void *workspace, size_t ws_bytes,
                            int32_t *dev_status, void *stream);
+
+/*
+ * A synthetic decoder for wedlm_model_step: per layer the pre-norm block
+ *   h = RMSNorm(x) * attn_norm;  q, k, v = h Wq^T, h Wk^T, h Wv^T
+ *   x += (windowed causal attention of the reordered window, as
+ *         wedlm_reorder + wedlm_step_attn on this layer's cache) Wo^T
+ *   h = RMSNorm(x) * mlp_norm;  x += (silu(h Wg^T) * (h Wu^T)) Wd^T
+ * (TL;DR of the paper-summary page: a Qwen3-8B backbone; the block itself
+ * is this library's plain reading.)  All weights bf16, row-major with the
+ * input dimension contiguous: wq [Hq*D][d_model], wk, wv [Hkv*D][d_model],
+ * wo [d_model][Hq*D], w_gate, w_up [d_ff][d_model], w_down [d_model][d_ff];
+ * norms [d_model].  k_cache / v_cache: this layer's paged cache as for
+ * wedlm_reorder.
+ */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+    void *k_cache, *v_cache;
+} wedlm_layer_weights;
+
+typedef struct {
+    int32_t n_layers, d_model, d_ff, vocab;
+    float rms_eps;
+    const void *embed;        /* [vocab + 1][d_model] bf16; row vocab = the mask token */
+    const void *final_norm;   /* [d_model] bf16 */
+    const void *lm_head;      /* [vocab][d_model] bf16 */
+    const wedlm_layer_weights *layers;   /* host array of n_layers */
+} wedlm_model;
+
+/*
+ * wedlm_model_step_workspace -- bytes of device workspace for
+ * wedlm_model_step (activations, split-K partial products, attention and
+ * LM-head scratch); 0 if the shapes are not supported.
+ */
+size_t wedlm_model_step_workspace(const wedlm_model *m, const wedlm_shape *s, int32_t max_ctx_len);
+
+/*
+ * wedlm_model_step -- one WeDLM streaming decode step of a whole synthetic
+ * decoder: embed the window tokens (tok, logical order; masked slots hold
+ * mask_id = vocab), run every layer on its cache with the window reordered
+ * by `filled` and RoPE at `pos`, apply the final RMSNorm, then the fused LM
+ * head + commit / Eq. 11 select / refill of wedlm_lmhead_select_commit.
+ * (paper-summary page, "Method", inference paragraph, and "Key claims",
+ * sec. 4.1 and 5.2.)
+ *
+ *   s        B, W (<= 64), Hq, Hkv, D (64 or 128), page_size 16, max_pages,
+ *            num_pages of the layer caches; dtype WEDLM_BF16
+ *   block_table [B][max_pages], shared by every layer's cache
+ *   tok, filled, pos, ctx_len, n_commit, committed, argmax_out,
+ *   entropy_out, alpha, tau  as for wedlm_select_commit (mask_id = vocab)
+ *   hidden_out  [B][W][d_model] bf16 device out (the final normalised
+ *            hidden states) or NULL
+ *   rope_base, max_ctx_len   as for wedlm_reorder / wedlm_step_attn
+ * d_model = Hq * D; d_model and d_ff multiples of 256; B*W <= 4096.
+ * Device-side problems are OR-ed into *dev_status (may be NULL).
+ */
+int wedlm_model_step(const wedlm_model *m, const wedlm_shape *s, const int32_t *block_table, int32_t *tok,
+                     uint8_t *filled, int32_t *pos, int32_t *ctx_len, int32_t *n_commit, int32_t *committed,
+                     int32_t *argmax_out, float *entropy_out, void *hidden_out, float alpha, float tau,
+                     double rope_base, int32_t max_ctx_len, void *workspace, size_t ws_bytes,
+                     int32_t *dev_status, void *stream);
 
 /*
  * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for

@@ -271,6 +271,74 @@ def dual_stream_attention(qm, km, vm, qp, kp, vp, flags, block: int, dtype: str,
     return out[0], out[1]
 
 
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> fp32 -> bf16 (round to nearest even) -> float64: the value
+    a GPU kernel stores after accumulating in fp32."""
+    f = np.ascontiguousarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis, float64."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(g, np.float64)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def model_step(w: dict, caches, tok, filled, pos, ctx_len, alpha: float, tau: float, base: float, eps: float,
+               Hq: int, Hkv: int, storage: str = "bf16"):
+    """One decode step of the synthetic decoder (float64; values stored by
+    the GPU in bf16 are rounded the same way when storage == "bf16").
+
+    The layer is the plain pre-norm decoder block (the pages name a
+    Qwen3-8B backbone, TL;DR, but not its layer; this is the reading):
+      x = E[tok];  per layer: h = RMSNorm(x) g_attn;  q, k, v = h W^T;
+      o = decode-step attention of the reordered window over the layer's
+      cache (reorder() + attention());  x += o Wo^T;  h = RMSNorm(x) g_mlp;
+      x += (silu(h Wg^T) * (h Wu^T)) Wd^T;  then RMSNorm(x) g_final, the LM
+      head and the select step (lmhead_select_commit()).
+    w: float64 weights (embed [V+1, d], final_norm, lm_head [V, d], layers
+    list of dicts).  caches[l] = (K list, V list) of per-sequence arrays
+    [>= ctx_len[b], Hkv, D] (rotated keys, logical order).  Returns the
+    select result plus "hidden" [B, W, d] and "caches" with the window's K/V
+    appended after ctx_len[b] in physical order."""
+    rnd = _round_bf16 if storage == "bf16" else (lambda a: np.asarray(a, np.float64))
+    dt = "bf16" if storage == "bf16" else "f64"
+    tok = np.asarray(tok)
+    B, W = tok.shape
+    layers = w["layers"]
+    D = layers[0]["wq"].shape[0] // Hq
+    ctx = np.asarray(ctx_len, np.int32)
+    x = np.asarray(w["embed"], np.float64)[tok]
+    h = rnd(rms_norm(x, layers[0]["attn_norm"], eps))
+    new_caches = []
+    for l, lw in enumerate(layers):
+        q = rnd(h @ lw["wq"].T).reshape(B, W, Hq, D)
+        k = rnd(h @ lw["wk"].T).reshape(B, W, Hkv, D)
+        v = rnd(h @ lw["wv"].T).reshape(B, W, Hkv, D)
+        perm, qp, kw, vw = reorder(filled, pos, q, k, v, dt, base)
+        dk = [np.concatenate([caches[l][0][b][:ctx[b]], kw[b]], axis=0) for b in range(B)]
+        dv = [np.concatenate([caches[l][1][b][:ctx[b]], vw[b]], axis=0) for b in range(B)]
+        o = rnd(attention(qp, dk, dv, ctx, perm)).reshape(B, W, Hq * D)
+        x = x + o @ lw["wo"].T
+        h = rnd(rms_norm(x, lw["mlp_norm"], eps))
+        act = rnd(silu(h @ lw["w_gate"].T) * (h @ lw["w_up"].T))
+        x = x + act @ lw["w_down"].T
+        nxt = layers[l + 1]["attn_norm"] if l + 1 < len(layers) else w["final_norm"]
+        h = rnd(rms_norm(x, nxt, eps))
+        new_caches.append((dk, dv))
+    V = w["lm_head"].shape[0]
+    out = lmhead_select_commit(h, w["lm_head"], tok, filled, pos, ctx, alpha, tau, V)
+    out["hidden"] = h
+    out["caches"] = new_caches
+    return out
+
+
 def decode_step_attention(inp, scale: Optional[float] = None, rows=None):
     """Oracle for reorder + attention on one batch drawn by
     workloads.make_attn_inputs.  Returns a dict

@@ -117,6 +117,43 @@ LMHEAD_CONFIGS: Dict[str, LmheadConfig] = {
 }
 
 
+@dataclass(frozen=True)
+class ModelConfig:
+    """A synthetic decoder for the whole-step path: `layers` pre-norm blocks
+    of d_model = Hq * D, GQA attention, SwiGLU MLP of width d_ff."""
+    name: str
+    layers: int
+    Hq: int
+    Hkv: int
+    D: int
+    d_ff: int
+    vocab: int
+    B: int
+    W: int
+    seed: int
+    alpha: float
+    tau: float
+    rope_base: float = 1e6
+    eps: float = 1e-6
+    steps: int = 1
+
+    @property
+    def d_model(self) -> int:
+        return self.Hq * self.D
+
+
+MODEL_CONFIGS: Dict[str, ModelConfig] = {
+    "model_small": ModelConfig("model_small", layers=2, Hq=4, Hkv=2, D=64, d_ff=512, vocab=1000, B=2, W=8,
+                               seed=1501, alpha=0.25, tau=float(np.log(1000) * 0.8), steps=6),
+    "model_qwen3_layer": ModelConfig("model_qwen3_layer", layers=1, Hq=32, Hkv=8, D=128, d_ff=12288, vocab=32000,
+                                     B=4, W=64, seed=1502, alpha=0.25, tau=float(np.log(32000) * 0.8)),
+    # Qwen3-8B shapes: 36 layers, hidden 4096, 32/8 heads of 128, MLP 12288,
+    # vocabulary 151936; batch 4 x the pages' window N = 64
+    "model_qwen3_w64": ModelConfig("model_qwen3_w64", layers=36, Hq=32, Hkv=8, D=128, d_ff=12288,
+                                   vocab=151936, B=4, W=64, seed=1503, alpha=0.25, tau=9.0, steps=16),
+}
+
+
 SELECT_CONFIGS: Dict[str, SelectConfig] = {
     "tiny_f32": SelectConfig("tiny_f32", B=1, W=8, V=1000, seed=1001, alpha=0.25, tau=4.5,
                              steps=1, kind="normal_scaled", scale=2.0),
@@ -396,6 +433,57 @@ def make_hidden_torch(cfg: LmheadConfig, step: int, lm_head, device):
     spike = 12.0 * wk / (wk * wk).sum(dim=-1, keepdim=True)
     h += torch.where(low[..., None], spike, torch.zeros_like(spike))
     return h.to(torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
+# synthetic decoder weights (bf16)
+# ----------------------------------------------------------------------------
+def _model_shapes(cfg: ModelConfig):
+    d, F, q, kv = cfg.d_model, cfg.d_ff, cfg.Hq * cfg.D, cfg.Hkv * cfg.D
+    layer = [("attn_norm", (d,), None), ("wq", (q, d), d), ("wk", (kv, d), d), ("wv", (kv, d), d),
+             ("wo", (d, q), q), ("mlp_norm", (d,), None), ("w_gate", (F, d), d), ("w_up", (F, d), d),
+             ("w_down", (d, F), F)]
+    top = [("embed", (cfg.vocab + 1, d), 0), ("final_norm", (d,), None), ("lm_head", (cfg.vocab, d), d)]
+    return top, layer
+
+
+def make_model_np(cfg: ModelConfig) -> dict:
+    """Weights as bf16 bits: embeddings N(0,1); norm weights 1 + 0.1 N(0,1);
+    every projection N(0, 1/fan_in)."""
+    rng = np.random.default_rng(cfg.seed)
+    top, layer = _model_shapes(cfg)
+
+    def draw(shape, fan_in):
+        x = _normal(rng, shape)
+        if fan_in is None:
+            x = np.float32(1.0) + np.float32(0.1) * x
+        elif fan_in:
+            x *= np.float32(1.0 / np.sqrt(fan_in))
+        return f32_to_bf16_bits(x)
+
+    out = {n: draw(sh, f) for n, sh, f in top}
+    out["layers"] = [{n: draw(sh, f) for n, sh, f in layer} for _ in range(cfg.layers)]
+    return out
+
+
+def make_model_torch(cfg: ModelConfig, device) -> dict:
+    """Device draw of the same recipe (torch's generator, seed = cfg.seed)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+    top, layer = _model_shapes(cfg)
+
+    def draw(shape, fan_in):
+        x = torch.empty(shape, dtype=torch.float32, device=device).normal_(generator=g)
+        if fan_in is None:
+            x = 1.0 + 0.1 * x
+        elif fan_in:
+            x *= 1.0 / float(np.sqrt(fan_in))
+        return x.to(torch.bfloat16)
+
+    out = {n: draw(sh, f) for n, sh, f in top}
+    out["layers"] = [{n: draw(sh, f) for n, sh, f in layer} for _ in range(cfg.layers)]
+    return out
 
 
 # ----------------------------------------------------------------------------
