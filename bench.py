@@ -53,11 +53,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_b4",
                     choices=["long_b4", "ragged_b32", "qwen3_l2048", "tiny_f32", "select_v152k",
-                             "lmhead_v152k", "dualstream_n4096"],
+                             "lmhead_v152k", "dualstream_n4096", "model_qwen3_w64"],
                     help="select_v152k times the select/commit call alone (batch 64 x window 16, "
                          "V=151936, streaming from an all-masked window); lmhead_v152k the fused "
                          "LM head + select call (hidden 4096) on the same window; dualstream_n4096 the "
-                         "Dual-Stream Masking attention over 4 x 4096 tokens, blocks of 32")
+                         "Dual-Stream Masking attention over 4 x 4096 tokens, blocks of 32; model_qwen3_w64 "
+                         "whole decode steps of a 36-layer Qwen3-8B-shaped synthetic decoder on a 4 x 64 window")
     ap.add_argument("--vocab", type=int, default=151936)
     ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
@@ -108,6 +109,9 @@ def main():
         return
     if args.workload == "dualstream_n4096":
         bench_dual(args)
+        return
+    if args.workload == "model_qwen3_w64":
+        bench_model(args)
         return
 
     import torch
@@ -599,6 +603,182 @@ def bench_dual(args):
                                                           for x in (qm, km, vm, qp, kp, vp)],
                                                    flags[:1].cpu().numpy(), b)
     print(json.dumps(result), flush=True)
+
+
+def bench_model(args):
+    """Whole decode steps of the synthetic decoder (wedlm_model_step):
+    Qwen3-8B shapes (36 layers, hidden 4096, 32 / 8 heads of 128, SwiGLU
+    12288, vocabulary 151936), random bf16 weights (embeddings N(0,1),
+    projections N(0, 1/fan_in), norms 1 + 0.1 N(0,1)), batch 4 x window 64,
+    each sequence with a 2048-token cached prompt (K/V N(0,1) bf16 in
+    shuffled 16-token pages).  Steps stream from an all-masked window."""
+    import torch
+    import workloads as wl
+    import causal_attention_diffusion_amd as wd
+
+    dev = torch.device("cuda:0")
+    cfg = wl.MODEL_CONFIGS["model_qwen3_w64"]
+    B, W, L0 = cfg.B, cfg.W, cfg.prefix
+    total = args.warmup + args.steps
+    max_ctx = L0 + total * W
+    mp = (max_ctx + W + 15) // 16
+    pool = B * mp
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 11)
+    w = wl.make_model_torch(cfg, dev)
+    for lw in w["layers"]:
+        lw["k_cache"] = torch.randn((pool, cfg.Hkv, 16, cfg.D), generator=g, device=dev).to(torch.bfloat16)
+        lw["v_cache"] = torch.randn((pool, cfg.Hkv, 16, cfg.D), generator=g, device=dev).to(torch.bfloat16)
+    bt = torch.randperm(pool, generator=g, device=dev).to(torch.int32).reshape(B, mp)
+    handle = wd.ModelHandle(w, cfg.eps)
+    shape = wd.make_shape(B, W, cfg.Hq, cfg.Hkv, cfg.D, mp, pool, wd.WEDLM_BF16)
+    ws = wd.model_step_workspace_tensor(handle, shape, max_ctx, dev)
+    init = [torch.from_numpy(x).to(dev) for x in wl.initial_window(B, W, cfg.vocab, L0)]
+    tok, filled, pos, ctx = [x.clone() for x in init]
+    n_commit_hist = torch.zeros((total, B), dtype=torch.int32, device=dev)
+    committed = torch.empty((B, W), dtype=torch.int32, device=dev)
+    argmax_hist = torch.empty((total, B, W), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(i):
+        wd.wedlm_model_step(handle, shape, bt, tok, filled, pos, ctx, n_commit_hist[i], committed, cfg.alpha,
+                            cfg.tau, cfg.rope_base, max_ctx, ws, argmax_out=argmax_hist[i], dev_status=status)
+
+    def reset():
+        for x, y in zip((tok, filled, pos, ctx), init):
+            x.copy_(y)
+
+    for i in range(args.warmup):
+        step(i)
+    reset()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.warmup, total):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    eager_elapsed = time.perf_counter() - t0
+    call_ms = ev0.elapsed_time(ev1) / args.steps
+    if status.item() != 0:
+        print(f"device status {status.item()}", file=sys.stderr)
+        sys.exit(3)
+    ctx_eager = ctx.clone()
+    state_eager = [x.clone() for x in (tok, filled, pos, ctx)]
+    elapsed = eager_elapsed
+    if not args.eager:
+        reset()
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(args.warmup, total):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(2):
+            reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+        for x, y in zip((tok, filled, pos, ctx), state_eager):
+            if not torch.equal(x, y):
+                print("graph replay diverged from the eager steps", file=sys.stderr)
+                sys.exit(3)
+
+    K = args.steps
+    ms_step = elapsed * 1e3 / K
+    d, F, V, Lyr = cfg.d_model, cfg.d_ff, cfg.vocab, cfg.layers
+    kvw = cfg.Hkv * cfg.D
+    layer_params = 2 * d * d + 2 * kvw * d + 3 * F * d
+    masked = (argmax_hist[args.warmup:] >= 0).sum(dim=(1, 2)).cpu().numpy().astype(np.float64)
+    nc = n_commit_hist[args.warmup:].cpu().numpy().astype(np.int64)
+    # context of the timed steps: L0 at the first, then growing by the commits
+    ctx_start = L0 + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(nc, 0)[:-1]], 0)
+    keys_mean = float((ctx_start + W).sum(1).mean())
+    # algorithmic bytes per step: every weight once (layers, final norm, LM
+    # head), the window rows of the embedding, every layer's cached K/V of
+    # each visible key once and the window's K/V appended
+    alg_bytes = (Lyr * (layer_params + 2 * d) + d + V * d + B * W * d) * 2.0 \
+        + Lyr * (keys_mean * kvw * 2 * 2 + B * W * kvw * 2 * 2)
+    flops = Lyr * 2.0 * B * W * layer_params + 2.0 * float(masked.mean()) * d * V \
+        + Lyr * 4.0 * cfg.Hq * cfg.D * W * keys_mean
+    gbs = alg_bytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(B * W / (ms_step * 1e-3), 1),
+        "unit": "window tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights)", "graph": not args.eager,
+        "eager_ms_per_step": round(eager_elapsed * 1e3 / K, 4),
+        "config": {"workload": f"model_qwen3_w64: {Lyr}-layer synthetic decoder of Qwen3-8B shapes (hidden {d}, "
+                               f"{cfg.Hq}/{cfg.Hkv} heads of {cfg.D}, MLP {F}, vocab {V}), B={B} x W={W} window, "
+                               f"{L0}-token cached prompt, {K} streaming steps from an all-masked window",
+                   "batch": B, "window": W, "layers": Lyr, "hidden": d, "vocab": V, "prompt": L0},
+        "steps_per_s": round(1e3 / ms_step, 2),
+        "model_step": {"avg_ms": round(call_ms, 5), "alg_bytes_per_step": int(alg_bytes),
+                       "GB_per_s": round(gbs, 1), "alg_flops_per_step": int(flops),
+                       "TFLOP_per_s": round(flops / (call_ms * 1e-3) / 1e12, 1),
+                       "masked_rows_per_step": round(float(masked.mean()), 2),
+                       "final_ctx": ctx_eager.cpu().tolist()},
+        "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
+        "P_c": round(float(nc.sum()) / (K * B * W), 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "wedlm_model_step (all launches of one decode step)"},
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline_model(cfg, w, bt)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_model(cfg, w_dev, bt):
+    """The oracle's model step, untuned, on the host cores, for the first
+    sequence of the first step (64 masked rows after the 2048-token prompt),
+    on the bench's own bf16 weights and caches copied to the host.  It runs
+    with the first layer, then the first two; the 36-layer step time is
+    t(2) + 34 (t(2) - t(1))."""
+    import oracle
+    import workloads as wl
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    L0, W = cfg.prefix, cfg.W
+    top = {"embed": host(w_dev["embed"]), "final_norm": host(w_dev["final_norm"]),
+           "lm_head": host(w_dev["lm_head"])}
+    layers, caches = [], []
+    import torch
+    t = torch.arange(L0, device=bt.device)
+    pg = bt[0].long()[t // 16], t % 16
+    for l in range(2):
+        lw = w_dev["layers"][l]
+        layers.append({k: host(v) for k, v in lw.items() if k not in ("k_cache", "v_cache")})
+        kc = lw["k_cache"][pg[0], :, pg[1], :]
+        vc = lw["v_cache"][pg[0], :, pg[1], :]
+        caches.append(([host(kc)], [host(vc)]))
+    tok, filled, pos, ctx = wl.initial_window(1, W, cfg.vocab, L0)
+    times = {}
+    for n in (1, 2):
+        wn = dict(top, layers=layers[:n])
+        best = None
+        for _ in range(2):
+            t0 = time.perf_counter()
+            oracle.model_step(wn, caches[:n], tok, filled, pos, ctx, cfg.alpha, cfg.tau, cfg.rope_base, cfg.eps,
+                              cfg.Hq, cfg.Hkv)
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        times[n] = best
+    est = times[2] + (cfg.layers - 2) * max(times[2] - times[1], 0.0)
+    return {"value": round(W / est, 3), "unit": "window tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"sequence 0 of the first step ({W} masked rows, {L0}-token prompt) with 1 and 2 layers "
+                      f"({times[1]:.2f} s, {times[2]:.2f} s, best of 2); {cfg.layers}-layer step estimated as "
+                      f"t2 + {cfg.layers - 2} (t2 - t1) = {est:.2f} s"}
 
 
 def cpu_baseline_dual(args, arrs, flags, b):

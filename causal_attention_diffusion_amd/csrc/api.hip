@@ -299,9 +299,9 @@ extern "C" int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32
 
 // ---------------------------------------------------------------- synthetic decoder step
 struct ModelLayout {
-    size_t x_res, h, q, k, v, qphys, perm, o, act, P1, P2, attn, lm, total;
+    size_t x_res, h, q, k, v, qphys, perm, o, act, P, attn, lm, total;
     size_t attn_bytes, lm_bytes;
-    int Sq, Skv, So, Sgu, Sd;
+    int Sqkv, So, Sgu, Sd;
 };
 
 static int model_layout(const wedlm_model* m, const wedlm_shape* s, int32_t max_ctx_len, ModelLayout* L) {
@@ -322,14 +322,13 @@ static int model_layout(const wedlm_model* m, const wedlm_shape* s, int32_t max_
     if (!lmhead_layout(s->B, s->W, m->vocab, m->d_model, &LL))
         return fail(WEDLM_ERR_SHAPE, "model: LM head shape not supported");
     const int d = m->d_model, F = m->d_ff, HqD = s->Hq * s->D, HkvD = s->Hkv * s->D;
-    L->Sq = gemm_splits((int)M, HqD, d);
-    L->Skv = gemm_splits((int)M, HkvD, d);
+    const int Nqkv = HqD + 2 * HkvD;
+    L->Sqkv = gemm_splits((int)M, Nqkv, d);
     L->So = gemm_splits((int)M, d, HqD);
-    L->Sgu = gemm_splits((int)M, F, d);
+    L->Sgu = gemm_splits((int)M, 2 * F, d);
     L->Sd = gemm_splits((int)M, d, F);
     size_t pmax = 0;
-    for (size_t x : {(size_t)L->Sq * HqD, (size_t)L->Skv * HkvD, (size_t)L->So * d, (size_t)L->Sgu * F,
-                     (size_t)L->Sd * d})
+    for (size_t x : {(size_t)L->Sqkv * Nqkv, (size_t)L->So * d, (size_t)L->Sgu * 2 * F, (size_t)L->Sd * d})
         pmax = x > pmax ? x : pmax;
     pmax *= (size_t)M * 4;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -344,8 +343,7 @@ static int model_layout(const wedlm_model* m, const wedlm_shape* s, int32_t max_
     L->perm = take((size_t)M * 4);
     L->o = take((size_t)M * HqD * 2);
     L->act = take((size_t)M * F * 2);
-    L->P1 = take(pmax);
-    L->P2 = take(pmax);
+    L->P = take(pmax);
     L->attn_bytes = make_plan(s, max_ctx_len).ws_bytes;
     L->attn = take(L->attn_bytes);
     L->lm_bytes = LL.total;
@@ -374,7 +372,13 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
         if (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.wo || !w.mlp_norm || !w.w_gate || !w.w_up || !w.w_down ||
             !w.k_cache || !w.v_cache)
             return fail(WEDLM_ERR_ARG, "wedlm_model_step: layer %d has a NULL pointer", l);
+        for (const void* p : {w.attn_norm, w.wq, w.wk, w.wv, w.wo, w.mlp_norm, w.w_gate, w.w_up, w.w_down})
+            if (reinterpret_cast<uintptr_t>(p) % 16)
+                return fail(WEDLM_ERR_ARG, "wedlm_model_step: layer %d weights must be 16-byte aligned", l);
     }
+    for (const void* p : {m->embed, m->final_norm, m->lm_head})
+        if (reinterpret_cast<uintptr_t>(p) % 16)
+            return fail(WEDLM_ERR_ARG, "wedlm_model_step: embed, final_norm and lm_head must be 16-byte aligned");
     if (!workspace || ws_bytes < L.total)
         return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, workspace ? ws_bytes : 0);
     char* ws = static_cast<char*>(workspace);
@@ -383,33 +387,35 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
     auto bf = [&](size_t off) { return reinterpret_cast<bf16_t*>(ws + off); };
     auto f32 = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     auto cbf = [](const void* p) { return static_cast<const bf16_t*>(p); };
-    auto gemm = [&](const void* W, const bf16_t* X, float* P, int N, int K, int S) {
-        GemmArgs g{cbf(W), X, P, M, N, K, S, 1};
+    // y = X W^T over up to three weight matrices stacked along the output
+    // dimension (rows [0, n1) of W0, [n1, n2) of W1, [n2, N) of W2)
+    auto gemm = [&](const void* W0, const void* W1, const void* W2, int n1, int n2, const bf16_t* X, int N, int K,
+                    int S) {
+        GemmArgs g{cbf(W0), cbf(W1), cbf(W2), n1, n2, X, f32(L.P), M, N, K, S, 1};
         return hip_status(launch_gemm(g, st), "wedlm_model_step gemm");
     };
-    auto rows = [&](const float* P, const float* Pg, bf16_t* out, int N, int S, const void* norm) {
+    auto rows = [&](bf16_t* out, int N, int S, const void* norm) {
         ModelRowArgs r{};
-        r.x_res = f32(L.x_res); r.h = out; r.g = cbf(norm); r.P = P; r.Pg = Pg;
+        r.x_res = f32(L.x_res); r.h = out; r.g = cbf(norm); r.P = f32(L.P);
         r.M = M; r.N = N; r.S = S; r.eps = m->rms_eps; r.status = dev_status;
         return r;
     };
     {
-        ModelRowArgs r = rows(nullptr, nullptr, bf(L.h), d, 0, m->layers[0].attn_norm);
+        ModelRowArgs r = rows(bf(L.h), d, 0, m->layers[0].attn_norm);
         r.tok = tok; r.embed = cbf(m->embed); r.n_embed = m->vocab + 1;
         rc = hip_status(launch_embed_rmsnorm(r, st), "wedlm_model_step embed");
         if (rc) return rc;
     }
+    const int Nqkv = HqD + 2 * HkvD;
     for (int l = 0; l < m->n_layers; ++l) {
         const wedlm_layer_weights& w = m->layers[l];
         const void* next_norm = l + 1 < m->n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        // q, k, v projections of the normalised window rows
-        struct { const void* W; size_t out; int N, S; } proj[3] = {
-            {w.wq, L.q, HqD, L.Sq}, {w.wk, L.k, HkvD, L.Skv}, {w.wv, L.v, HkvD, L.Skv}};
-        for (auto& pj : proj) {
-            if ((rc = gemm(pj.W, bf(L.h), f32(L.P1), pj.N, d, pj.S))) return rc;
-            if ((rc = hip_status(launch_finish_rows(rows(f32(L.P1), nullptr, bf(pj.out), pj.N, pj.S, nullptr), st),
-                                 "wedlm_model_step finish")))
-                return rc;
+        // q, k, v of the normalised window rows: one launch over [Wq; Wk; Wv]
+        if ((rc = gemm(w.wq, w.wk, w.wv, HqD, HqD + HkvD, bf(L.h), Nqkv, d, L.Sqkv))) return rc;
+        {
+            ModelRowArgs r = rows(bf(L.q), Nqkv, L.Sqkv, nullptr);
+            r.h1 = bf(L.k); r.h2 = bf(L.v); r.n1 = HqD; r.n2 = HqD + HkvD;
+            if ((rc = hip_status(launch_finish_split(r, st), "wedlm_model_step finish"))) return rc;
         }
         // reorder + RoPE + append into this layer's cache, then attention
         rc = wedlm_reorder(s, filled, pos, ws + L.q, ws + L.k, ws + L.v, ws + L.qphys, w.k_cache, w.v_cache,
@@ -420,19 +426,17 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
                              L.attn_bytes, dev_status, stream);
         if (rc) return rc;
         // x += o Wo^T; h = RMSNorm(x) * mlp_norm
-        if ((rc = gemm(w.wo, bf(L.o), f32(L.P1), d, HqD, L.So))) return rc;
-        if ((rc = hip_status(launch_add_rmsnorm(rows(f32(L.P1), nullptr, bf(L.h), d, L.So, w.mlp_norm), st),
-                             "wedlm_model_step norm")))
+        if ((rc = gemm(w.wo, w.wo, w.wo, d, d, bf(L.o), d, HqD, L.So))) return rc;
+        if ((rc = hip_status(launch_add_rmsnorm(rows(bf(L.h), d, L.So, w.mlp_norm), st), "wedlm_model_step norm")))
             return rc;
-        // act = silu(h Wg^T) * (h Wu^T); x += act Wd^T; h = RMSNorm(x) * next norm
-        if ((rc = gemm(w.w_gate, bf(L.h), f32(L.P2), F, d, L.Sgu))) return rc;
-        if ((rc = gemm(w.w_up, bf(L.h), f32(L.P1), F, d, L.Sgu))) return rc;
-        if ((rc = hip_status(launch_finish_rows(rows(f32(L.P1), f32(L.P2), bf(L.act), F, L.Sgu, nullptr), st),
+        // act = silu(h Wg^T) * (h Wu^T): one launch over [Wg; Wu]
+        if ((rc = gemm(w.w_gate, w.w_up, w.w_up, F, 2 * F, bf(L.h), 2 * F, d, L.Sgu))) return rc;
+        if ((rc = hip_status(launch_finish_swiglu(rows(bf(L.act), 2 * F, L.Sgu, nullptr), st),
                              "wedlm_model_step finish")))
             return rc;
-        if ((rc = gemm(w.w_down, bf(L.act), f32(L.P1), d, F, L.Sd))) return rc;
-        if ((rc = hip_status(launch_add_rmsnorm(rows(f32(L.P1), nullptr, bf(L.h), d, L.Sd, next_norm), st),
-                             "wedlm_model_step norm")))
+        // x += act Wd^T; h = RMSNorm(x) * next norm
+        if ((rc = gemm(w.w_down, w.w_down, w.w_down, d, d, bf(L.act), d, F, L.Sd))) return rc;
+        if ((rc = hip_status(launch_add_rmsnorm(rows(bf(L.h), d, L.Sd, next_norm), st), "wedlm_model_step norm")))
             return rc;
     }
     if (hidden_out) {

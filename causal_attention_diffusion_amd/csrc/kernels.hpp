@@ -94,16 +94,23 @@ struct ModelRowArgs {
     const bf16_t* embed;    // embed: [n_embed][N]
     int n_embed;
     float* x_res;           // residual stream [M][N] fp32
-    bf16_t* h;              // bf16 output [M][N]
+    bf16_t* h;              // bf16 output [M][N] (split finish: columns [0, n1))
+    bf16_t* h1;             // split finish: columns [n1, n2) as [M][n2 - n1]
+    bf16_t* h2;             // split finish: columns [n2, N) as [M][N - n2]
+    int n1, n2;
     const bf16_t* g;        // RMSNorm weight [N]
-    const float* P;         // split-K partials [S][M][N]
-    const float* Pg;        // gate partials for the SwiGLU finish, or nullptr
+    const float* P;         // split-K partials [S][M][N] (SwiGLU: N = 2F, gate then up)
     int M, N, S;
     float eps;
     int32_t* status;
 };
+// y = X W^T for W stacked from up to three matrices along the output
+// dimension: rows [0, n1) of W0, [n1, n2) of W1, [n2, N) of W2.
 struct GemmArgs {
-    const bf16_t* W;        // [N][K]
+    const bf16_t* W0;       // [n1][K]
+    const bf16_t* W1;       // [n2 - n1][K] (or unused when n1 == N)
+    const bf16_t* W2;       // [N - n2][K]  (or unused when n2 == N)
+    int n1, n2;
     const bf16_t* X;        // [M][K]
     float* P;               // [S][M][N] partial products
     int M, N, K, S, nrg;    // nrg set by the launcher
@@ -112,7 +119,8 @@ int gemm_splits(int M, int N, int K);
 hipError_t launch_gemm(GemmArgs a, hipStream_t stream);
 hipError_t launch_embed_rmsnorm(const ModelRowArgs& a, hipStream_t stream);
 hipError_t launch_add_rmsnorm(const ModelRowArgs& a, hipStream_t stream);
-hipError_t launch_finish_rows(const ModelRowArgs& a, hipStream_t stream);
+hipError_t launch_finish_split(const ModelRowArgs& a, hipStream_t stream);
+hipError_t launch_finish_swiglu(const ModelRowArgs& a, hipStream_t stream);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
 hipError_t launch_dual_layout(uint8_t* filled_m, int32_t* pos_m, int32_t* ctx_m, int32_t* bt_m, int32_t* pos_p,
                               int32_t* ctx_p, int32_t* bt_p, int S, int N, int b, hipStream_t stream);

@@ -54,14 +54,36 @@ __device__ __forceinline__ void tile_block_sync() {
 }
 
 // acc = A[n0 .. n0+NT) . B[rows]^T over K elements (a multiple of KC) of
-// rows ld elements long (A and B point at the first element of the K
-// range).  A rows at or past n_lim repeat row n_lim - 1 (the caller ignores
-// their results); B rows are s_rows[0 .. MT) (LDS, set and synchronised by
-// the caller).  s_ring: C::SLOTS * C::SLOTB bytes of LDS.  Ends with a
-// barrier-free ring: the caller synchronises before reusing s_ring.
-template <class C>
-__device__ __forceinline__ void tile_mma(const char* A, int n0, int n_lim, const char* Bm, const int* s_rows, int K,
-                                         int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM]) {
+// rows ld elements long (arows(n) and B point at the first element of the
+// K range of their row).  A rows at or past n_lim repeat row n_lim - 1 (the
+// caller ignores their results); B rows are s_rows[0 .. MT) (LDS, set and
+// synchronised by the caller).  s_ring: C::SLOTS * C::SLOTB bytes of LDS.
+// Ends with a barrier-free ring: the caller synchronises before reusing
+// s_ring.
+// A row addresses: row n of a single matrix of `rowbytes`-long rows.
+struct PlainRows {
+    const char* A;
+    size_t rowbytes;
+    __device__ const char* operator()(int n) const { return A + (size_t)n * rowbytes; }
+};
+
+// A rows stacked from up to three matrices with the same row length: rows
+// [0, n1) of p0, then [n1, n2) of p1, then the rest of p2.
+struct StackedRows {
+    const char* p0;
+    const char* p1;
+    const char* p2;
+    int n1, n2;
+    size_t rowbytes;
+    __device__ const char* operator()(int n) const {
+        return n < n1 ? p0 + (size_t)n * rowbytes
+                      : (n < n2 ? p1 + (size_t)(n - n1) * rowbytes : p2 + (size_t)(n - n2) * rowbytes);
+    }
+};
+
+template <class C, class ARows>
+__device__ __forceinline__ void tile_mma_rows(const ARows& arows, int n0, int n_lim, const char* Bm, const int* s_rows,
+                                         int K, int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM]) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -80,7 +102,7 @@ __device__ __forceinline__ void tile_mma(const char* A, int n0, int n_lim, const
         if (q < C::NT / C::RPI) {
             const int row = q * C::RPI + lane / C::CPR;
             const int n = min(n0 + row, n_lim - 1);
-            gsrc[u] = A + (size_t)n * rowbytes + C::swz(row, p) * 16;
+            gsrc[u] = arows(n) + C::swz(row, p) * 16;
             ldst[u] = q * 1024;
         } else {
             const int m = (q - C::NT / C::RPI) * C::RPI + lane / C::CPR;
@@ -143,6 +165,13 @@ __device__ __forceinline__ void tile_mma(const char* A, int n0, int n_lim, const
                     acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[x], bf[y], acc[x][y], 0, 0, 0);
         }
     }
+}
+
+// The same over a single A matrix.
+template <class C>
+__device__ __forceinline__ void tile_mma(const char* A, int n0, int n_lim, const char* Bm, const int* s_rows, int K,
+                                         int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM]) {
+    tile_mma_rows<C>(PlainRows{A, (size_t)ld * 2}, n0, n_lim, Bm, s_rows, K, ld, s_ring, acc);
 }
 
 }  // namespace wedlm

@@ -14,17 +14,63 @@
 // Storage points: the residual stream x is fp32; normalised activations,
 // projections, attention outputs and the MLP activation are bf16 (the
 // GEMM operands).  A projection y = h W^T is computed as S split-K partial
-// products in fp32 (one work-group per (256-wide output tile, row group,
-// K split)), summed by the kernel that consumes it.
+// products in fp32 (one work-group per (output tile, row group, K split)),
+// summed by the kernel that consumes it.  q, k and v are one launch over
+// the three weight matrices stacked along the output dimension, and so are
+// the gate and up projections of the MLP.
 #include "kernels.hpp"
 #include "mma_tile.hpp"
 
 namespace wedlm {
 
-using GemmSmall = TileCfg<256, 128, 64, 3, 4>;   // up to 128 rows
-using GemmLarge = TileCfg<256, 256, 32, 4, 2>;   // 129 .. 256 rows per row group
+// up to 128 rows: 256 output columns x all rows per work-group
+using GemmSmall = TileCfg<256, 128, 64, 3, 4>;
+// more rows (the pages' window of 64 over a few sequences): 128 output
+// columns x 256 rows per work-group, so a projection of a few thousand
+// outputs splits K at most 8 ways to fill the chip and the fp32 partials
+// stay small next to the weights
+using GemmRows = TileCfg<128, 256, 64, 3, 2>;
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// four floats -> four bf16 (round to nearest even) as one 8-byte store
+__device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    return o;
+}
+__device__ __forceinline__ float4 unpack_bf16x4(uint2 u) {
+    return make_float4(bf16_to_f32(u.x & 0xffff), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffff),
+                       bf16_to_f32(u.y >> 16));
+}
+
+// Sum over the 256 threads of a work-group (4 waves).
+__device__ __forceinline__ float block_sum256(float v, float* s_red) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+// h[m] = RMSNorm(x_res[m]) * g (bf16), x_res[m] already final; every
+// thread owns the float4 columns tid, tid + 256, ...
+__device__ __forceinline__ void rmsnorm_row(const ModelRowArgs& a, int m, float ss, float* s_red) {
+    const int N4 = a.N / 4;
+    const float rs = rsqrtf(block_sum256(ss, s_red) / a.N + a.eps);
+    const float4* x = reinterpret_cast<const float4*>(a.x_res + (size_t)m * a.N);
+    const uint2* g = reinterpret_cast<const uint2*>(a.g);
+    uint2* h = reinterpret_cast<uint2*>(a.h + (size_t)m * a.N);
+    for (int c = threadIdx.x; c < N4; c += 256) {
+        const float4 v = x[c];
+        const float4 w = unpack_bf16x4(g[c]);
+        h[c] = pack_bf16x4(make_float4(v.x * rs * w.x, v.y * rs * w.y, v.z * rs * w.z, v.w * rs * w.w));
+    }
+}
 
 // x_res[m] = E[tok[m]] (fp32); h[m] = RMSNorm(x_res[m]) * g (bf16).
 // One work-group per row.
@@ -36,64 +82,100 @@ __global__ __launch_bounds__(256) void embed_rmsnorm(ModelRowArgs a) {
         if (threadIdx.x == 0) set_status(a.status, WEDLM_DEV_BAD_TOKEN);
         t = 0;
     }
-    const bf16_t* e = a.embed + (size_t)t * a.N;
-    float* x = a.x_res + (size_t)m * a.N;
+    const int N4 = a.N / 4;
+    const uint2* e = reinterpret_cast<const uint2*>(a.embed + (size_t)t * a.N);
+    float4* x = reinterpret_cast<float4*>(a.x_res + (size_t)m * a.N);
     float ss = 0.f;
-    for (int n = threadIdx.x; n < a.N; n += 256) {
-        const float v = bf16_to_f32(e[n].bits);
-        x[n] = v;
-        ss += v * v;
+    for (int c = threadIdx.x; c < N4; c += 256) {
+        const float4 v = unpack_bf16x4(e[c]);
+        x[c] = v;
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float rs = rsqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / a.N + a.eps);
-    bf16_t* h = a.h + (size_t)m * a.N;
-    for (int n = threadIdx.x; n < a.N; n += 256)
-        h[n].bits = f32_to_bf16(x[n] * rs * bf16_to_f32(a.g[n].bits));
+    rmsnorm_row(a, m, ss, s_red);
 }
 
-// x_res[m] += sum_s P[s][m]; h[m] = RMSNorm(x_res[m]) * g (bf16).
+// x_res[m] += sum_s P[s][m] (in split order); h[m] = RMSNorm(x_res[m]) * g.
+// One work-group per row; a thread keeps 4 float4 columns in flight across
+// all splits.
 __global__ __launch_bounds__(256) void add_rmsnorm(ModelRowArgs a) {
     const int m = blockIdx.x;
     __shared__ float s_red[4];
-    float* x = a.x_res + (size_t)m * a.N;
-    const size_t plane = (size_t)a.M * a.N;
+    const int N4 = a.N / 4;
+    float4* x = reinterpret_cast<float4*>(a.x_res + (size_t)m * a.N);
+    const float4* P = reinterpret_cast<const float4*>(a.P) + (size_t)m * N4;
+    const size_t plane4 = (size_t)a.M * N4;
     float ss = 0.f;
-    for (int n = threadIdx.x; n < a.N; n += 256) {
-        float v = x[n];
-        for (int s = 0; s < a.S; ++s) v += a.P[s * plane + (size_t)m * a.N + n];
-        x[n] = v;
-        ss += v * v;
-    }
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float rs = rsqrtf((s_red[0] + s_red[1] + s_red[2] + s_red[3]) / a.N + a.eps);
-    bf16_t* h = a.h + (size_t)m * a.N;
-    for (int n = threadIdx.x; n < a.N; n += 256)
-        h[n].bits = f32_to_bf16(x[n] * rs * bf16_to_f32(a.g[n].bits));
-}
-
-// out[m][n] = bf16(sum_s P[s][m][n]) (gate == nullptr), or
-// out[m][n] = bf16(silu(sum_s Pg) * sum_s P) with Pg = gate partials.
-__global__ __launch_bounds__(256) void finish_rows(ModelRowArgs a) {
-    const size_t total = (size_t)a.M * a.N;
-    const size_t plane = total;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
-        float v = 0.f;
-        for (int s = 0; s < a.S; ++s) v += a.P[s * plane + i];
-        if (a.Pg) {
-            float g = 0.f;
-            for (int s = 0; s < a.S; ++s) g += a.Pg[s * plane + i];
-            v *= silu(g);
+    for (int c0 = 0; c0 < N4; c0 += 1024) {
+        float4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + j * 256 + threadIdx.x;
+            v[j] = c < N4 ? x[c] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        a.h[i].bits = f32_to_bf16(v);
+        for (int s = 0; s < a.S; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = c0 + j * 256 + threadIdx.x;
+                if (c < N4) v[j] = add4(v[j], P[s * plane4 + c]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + j * 256 + threadIdx.x;
+            if (c < N4) {
+                x[c] = v[j];
+                ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+            }
+        }
+    }
+    rmsnorm_row(a, m, ss, s_red);   // re-reads only this thread's own columns
+}
+
+// Sum of the S partials of four consecutive columns (4c .. 4c+3) of row m.
+__device__ __forceinline__ float4 sum_splits(const ModelRowArgs& a, size_t i4) {
+    const float4* P = reinterpret_cast<const float4*>(a.P);
+    const size_t plane4 = (size_t)a.M * a.N / 4;
+    float4 v = P[i4];
+    for (int s = 1; s < a.S; ++s) v = add4(v, P[s * plane4 + i4]);
+    return v;
+}
+
+// Stacked projection outputs: bf16(sum_s P[s][m][n]) to h (n < n1), h1
+// (n1 <= n < n2) or h2 (n >= n2), each row-major with its own width.
+__global__ __launch_bounds__(256) void finish_split(ModelRowArgs a) {
+    const int N4 = a.N / 4;
+    const size_t total4 = (size_t)a.M * N4;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (size_t)gridDim.x * 256) {
+        const int m = (int)(i / N4);
+        const int n = (int)(i - (size_t)m * N4) * 4;
+        const uint2 o = pack_bf16x4(sum_splits(a, i));
+        bf16_t* dst = n < a.n1 ? a.h + (size_t)m * a.n1 + n
+                               : (n < a.n2 ? a.h1 + (size_t)m * (a.n2 - a.n1) + (n - a.n1)
+                                           : a.h2 + (size_t)m * (a.N - a.n2) + (n - a.n2));
+        *reinterpret_cast<uint2*>(dst) = o;
     }
 }
 
-// P[s][m][n] = sum over the s-th K range of X[m][k] W[n][k], fp32.
-// Work-group i: split s = i % S, then row group, then output tile.
+// SwiGLU activation from the stacked gate / up projection (N = 2F columns,
+// gate first): h[m][n] = bf16(silu(gate[m][n]) * up[m][n]), n < F.
+__global__ __launch_bounds__(256) void finish_swiglu(ModelRowArgs a) {
+    const int F4 = a.N / 8;
+    const size_t total4 = (size_t)a.M * F4;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (size_t)gridDim.x * 256) {
+        const int m = (int)(i / F4);
+        const int c = (int)(i - (size_t)m * F4);
+        const size_t row4 = (size_t)m * (2 * F4);
+        const float4 g = sum_splits(a, row4 + c);
+        const float4 u = sum_splits(a, row4 + F4 + c);
+        reinterpret_cast<uint2*>(a.h)[i] =
+            pack_bf16x4(make_float4(silu(g.x) * u.x, silu(g.y) * u.y, silu(g.z) * u.z, silu(g.w) * u.w));
+    }
+}
+
+// P[s][m][n] = sum over the s-th K range of X[m][k] W[n][k], fp32, W the
+// stacked weight rows.  Work-group i: split s = i % S (so the work-groups of
+// one K range share an XCD when S divides 8 or 8 divides S), then row
+// group, then output tile.
 template <class C>
 __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) char s_ring[C::SLOTS * C::SLOTB];
@@ -109,9 +191,10 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
     __syncthreads();
     const int kr = a.K / a.S;
     const size_t k0b = (size_t)s * kr * 2;
+    const StackedRows rows{reinterpret_cast<const char*>(a.W0) + k0b, reinterpret_cast<const char*>(a.W1) + k0b,
+                           reinterpret_cast<const char*>(a.W2) + k0b, a.n1, a.n2, (size_t)a.K * 2};
     f32x16 acc[C::TN][C::TM];
-    tile_mma<C>(reinterpret_cast<const char*>(a.W) + k0b, n0, a.N, reinterpret_cast<const char*>(a.X) + k0b, s_rows,
-                kr, a.K, s_ring, acc);
+    tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X) + k0b, s_rows, kr, a.K, s_ring, acc);
     const int wn = C::wave_n(), wm = C::wave_m();
     const int hl = lane >> 5, col = lane & 31;
     float* P = a.P + (size_t)s * a.M * a.N;
@@ -132,13 +215,22 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
     }
 }
 
-// Split count and launch of one projection.
+// Split count of one projection: the largest power of two (at most 16)
+// that keeps the launch within one work-group per CU (256) -- or, for
+// the small tile, the smallest that reaches it -- with K ranges that are
+// whole stages and at least four of them.
 int gemm_splits(int M, int N, int K) {
-    const int nt = (N + 255) / 256;
-    const int mt = M <= GemmSmall::MT ? 1 : (M + GemmLarge::MT - 1) / GemmLarge::MT;
-    const int kc = M <= GemmSmall::MT ? GemmSmall::KC : GemmLarge::KC;
+    const bool small = M <= GemmSmall::MT;
+    const int nt = small ? (N + GemmSmall::NT - 1) / GemmSmall::NT : (N + GemmRows::NT - 1) / GemmRows::NT;
+    const int mt = small ? 1 : (M + GemmRows::MT - 1) / GemmRows::MT;
+    const int kc = small ? GemmSmall::KC : GemmRows::KC;
     int S = 1;
-    while (nt * mt * S < 256 && S < 16 && K % (2 * S * kc) == 0 && K / (2 * S) >= 4 * kc) S *= 2;
+    auto can_double = [&](int s) { return s < 16 && K % (2 * s * kc) == 0 && K / (2 * s) >= 4 * kc; };
+    if (small) {
+        while (nt * mt * S < 256 && can_double(S)) S *= 2;
+    } else {
+        while (nt * mt * 2 * S <= 256 && can_double(S)) S *= 2;
+    }
     return S;
 }
 
@@ -148,9 +240,9 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
         const unsigned g = (unsigned)(((a.N + GemmSmall::NT - 1) / GemmSmall::NT) * a.S);
         hipLaunchKernelGGL(gemm_split<GemmSmall>, dim3(g), dim3(64 * GemmSmall::NW), 0, st, a);
     } else {
-        a.nrg = (a.M + GemmLarge::MT - 1) / GemmLarge::MT;
-        const unsigned g = (unsigned)(((a.N + GemmLarge::NT - 1) / GemmLarge::NT) * a.nrg * a.S);
-        hipLaunchKernelGGL(gemm_split<GemmLarge>, dim3(g), dim3(64 * GemmLarge::NW), 0, st, a);
+        a.nrg = (a.M + GemmRows::MT - 1) / GemmRows::MT;
+        const unsigned g = (unsigned)(((a.N + GemmRows::NT - 1) / GemmRows::NT) * a.nrg * a.S);
+        hipLaunchKernelGGL(gemm_split<GemmRows>, dim3(g), dim3(64 * GemmRows::NW), 0, st, a);
     }
     return hipGetLastError();
 }
@@ -163,10 +255,16 @@ hipError_t launch_add_rmsnorm(const ModelRowArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(add_rmsnorm, dim3((unsigned)a.M), dim3(256), 0, st, a);
     return hipGetLastError();
 }
-hipError_t launch_finish_rows(const ModelRowArgs& a, hipStream_t st) {
-    const size_t total = (size_t)a.M * a.N;
-    const size_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(finish_rows, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, st, a);
+static unsigned row_blocks(size_t items) {
+    const size_t b = (items + 255) / 256;
+    return (unsigned)(b < 4096 ? b : 4096);
+}
+hipError_t launch_finish_split(const ModelRowArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(finish_split, dim3(row_blocks((size_t)a.M * a.N / 4)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_finish_swiglu(const ModelRowArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(finish_swiglu, dim3(row_blocks((size_t)a.M * a.N / 8)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

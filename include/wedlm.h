@@ -298,7 +298,8 @@ int wedlm_dual_stream_attn(const wedlm_shape *s, int32_t N, const void *qm, cons
  * input dimension contiguous: wq [Hq*D][d_model], wk, wv [Hkv*D][d_model],
  * wo [d_model][Hq*D], w_gate, w_up [d_ff][d_model], w_down [d_model][d_ff];
  * norms [d_model].  k_cache / v_cache: this layer's paged cache as for
- * wedlm_reorder.
+ * wedlm_reorder.  Every weight pointer (here and in wedlm_model) must be
+ * 16-byte aligned; wedlm_model_step returns WEDLM_ERR_ARG otherwise.
  */
 typedef struct {
     const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;

@@ -136,6 +136,7 @@ class ModelConfig:
     rope_base: float = 1e6
     eps: float = 1e-6
     steps: int = 1
+    prefix: int = 0     # cached prompt tokens per sequence before the first step
 
     @property
     def d_model(self) -> int:
@@ -150,7 +151,8 @@ MODEL_CONFIGS: Dict[str, ModelConfig] = {
     # Qwen3-8B shapes: 36 layers, hidden 4096, 32/8 heads of 128, MLP 12288,
     # vocabulary 151936; batch 4 x the pages' window N = 64
     "model_qwen3_w64": ModelConfig("model_qwen3_w64", layers=36, Hq=32, Hkv=8, D=128, d_ff=12288,
-                                   vocab=151936, B=4, W=64, seed=1503, alpha=0.25, tau=9.0, steps=16),
+                                   vocab=151936, B=4, W=64, seed=1503, alpha=0.25, tau=9.0, steps=16,
+                                   prefix=2048),
 }
 
 
