@@ -49,23 +49,31 @@ __device__ __forceinline__ float4 unpack_bf16x4(uint2 u) {
                        bf16_to_f32(u.y >> 16));
 }
 
-// Sum over the 256 threads of a work-group (4 waves).
-__device__ __forceinline__ float block_sum256(float v, float* s_red) {
+// Row kernels run one work-group of kRowThreads threads per row: a thread
+// owns the float4 columns tid, tid + kRowThreads, ... (one each at a
+// 4096-wide row), so 16 waves per row keep the partial reads in flight.
+constexpr int kRowThreads = 1024;
+
+// Sum over the work-group (kRowThreads / 64 waves).
+__device__ __forceinline__ float block_sum(float v, float* s_red) {
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
     if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
     __syncthreads();
-    return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRowThreads / 64; ++w) t += s_red[w];
+    return t;
 }
 
-// h[m] = RMSNorm(x_res[m]) * g (bf16), x_res[m] already final; every
-// thread owns the float4 columns tid, tid + 256, ...
+// h[m] = RMSNorm(x_res[m]) * g (bf16), x_res[m] already final and written
+// by this same thread for its own columns.
 __device__ __forceinline__ void rmsnorm_row(const ModelRowArgs& a, int m, float ss, float* s_red) {
     const int N4 = a.N / 4;
-    const float rs = rsqrtf(block_sum256(ss, s_red) / a.N + a.eps);
+    const float rs = rsqrtf(block_sum(ss, s_red) / a.N + a.eps);
     const float4* x = reinterpret_cast<const float4*>(a.x_res + (size_t)m * a.N);
     const uint2* g = reinterpret_cast<const uint2*>(a.g);
     uint2* h = reinterpret_cast<uint2*>(a.h + (size_t)m * a.N);
-    for (int c = threadIdx.x; c < N4; c += 256) {
+    for (int c = threadIdx.x; c < N4; c += kRowThreads) {
         const float4 v = x[c];
         const float4 w = unpack_bf16x4(g[c]);
         h[c] = pack_bf16x4(make_float4(v.x * rs * w.x, v.y * rs * w.y, v.z * rs * w.z, v.w * rs * w.w));
@@ -73,10 +81,9 @@ __device__ __forceinline__ void rmsnorm_row(const ModelRowArgs& a, int m, float 
 }
 
 // x_res[m] = E[tok[m]] (fp32); h[m] = RMSNorm(x_res[m]) * g (bf16).
-// One work-group per row.
-__global__ __launch_bounds__(256) void embed_rmsnorm(ModelRowArgs a) {
+__global__ __launch_bounds__(kRowThreads) void embed_rmsnorm(ModelRowArgs a) {
     const int m = blockIdx.x;
-    __shared__ float s_red[4];
+    __shared__ float s_red[kRowThreads / 64];
     int t = a.tok[m];
     if (t < 0 || t >= a.n_embed) {
         if (threadIdx.x == 0) set_status(a.status, WEDLM_DEV_BAD_TOKEN);
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(256) void embed_rmsnorm(ModelRowArgs a) {
     const uint2* e = reinterpret_cast<const uint2*>(a.embed + (size_t)t * a.N);
     float4* x = reinterpret_cast<float4*>(a.x_res + (size_t)m * a.N);
     float ss = 0.f;
-    for (int c = threadIdx.x; c < N4; c += 256) {
+    for (int c = threadIdx.x; c < N4; c += kRowThreads) {
         const float4 v = unpack_bf16x4(e[c]);
         x[c] = v;
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -95,38 +102,19 @@ __global__ __launch_bounds__(256) void embed_rmsnorm(ModelRowArgs a) {
 }
 
 // x_res[m] += sum_s P[s][m] (in split order); h[m] = RMSNorm(x_res[m]) * g.
-// One work-group per row; a thread keeps 4 float4 columns in flight across
-// all splits.
-__global__ __launch_bounds__(256) void add_rmsnorm(ModelRowArgs a) {
+__global__ __launch_bounds__(kRowThreads) void add_rmsnorm(ModelRowArgs a) {
     const int m = blockIdx.x;
-    __shared__ float s_red[4];
+    __shared__ float s_red[kRowThreads / 64];
     const int N4 = a.N / 4;
     float4* x = reinterpret_cast<float4*>(a.x_res + (size_t)m * a.N);
     const float4* P = reinterpret_cast<const float4*>(a.P) + (size_t)m * N4;
     const size_t plane4 = (size_t)a.M * N4;
     float ss = 0.f;
-    for (int c0 = 0; c0 < N4; c0 += 1024) {
-        float4 v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = c0 + j * 256 + threadIdx.x;
-            v[j] = c < N4 ? x[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        for (int s = 0; s < a.S; ++s) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = c0 + j * 256 + threadIdx.x;
-                if (c < N4) v[j] = add4(v[j], P[s * plane4 + c]);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = c0 + j * 256 + threadIdx.x;
-            if (c < N4) {
-                x[c] = v[j];
-                ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-            }
-        }
+    for (int c = threadIdx.x; c < N4; c += kRowThreads) {
+        float4 v = x[c];
+        for (int s = 0; s < a.S; ++s) v = add4(v, P[s * plane4 + c]);
+        x[c] = v;
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
     rmsnorm_row(a, m, ss, s_red);   // re-reads only this thread's own columns
 }
@@ -248,11 +236,11 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
 }
 
 hipError_t launch_embed_rmsnorm(const ModelRowArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(embed_rmsnorm, dim3((unsigned)a.M), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(embed_rmsnorm, dim3((unsigned)a.M), dim3(kRowThreads), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_add_rmsnorm(const ModelRowArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(add_rmsnorm, dim3((unsigned)a.M), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(add_rmsnorm, dim3((unsigned)a.M), dim3(kRowThreads), 0, st, a);
     return hipGetLastError();
 }
 static unsigned row_blocks(size_t items) {
