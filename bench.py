@@ -152,9 +152,13 @@ def main():
         wd.wedlm_step_attn(t["q_phys"], t["k_cache"], t["v_cache"], t["block_table"], ctx, t["perm"],
                            t["out"], max_ctx_len=max_ctx, workspace=ws_attn, dev_status=t["status"])
 
+    # prefix-cacheability counters (N_new, N_total) kept by the select call
+    counters = torch.zeros((B, 2), dtype=torch.int64, device=dev)
+
     def select(i):
         wd.wedlm_select_commit(logits[i % len(logits)], tok, filled, pos, ctx, n_commit_hist[i], committed,
-                               scfg.alpha, scfg.tau, mask_id, ws_sel, argmax_out=argmax_hist[i])
+                               scfg.alpha, scfg.tau, mask_id, ws_sel, argmax_out=argmax_hist[i],
+                               counters=counters)
 
     def step(i):
         reorder()
@@ -172,6 +176,7 @@ def main():
     # untimed and once timed.  Capture records without running; a replay from
     # the same state rewrites the same cache rows with the same bytes.
     state0 = [x.clone() for x in (tok, filled, pos, ctx)]
+    counters.zero_()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.warmup, total_steps):
@@ -193,11 +198,13 @@ def main():
         for _ in range(2):
             for x, y in zip((tok, filled, pos, ctx), state0):
                 x.copy_(y)
+            counters.zero_()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             graph.replay()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - t0
+    cnt = counters.cpu().numpy()
 
     # ---- timed region 2: the attention call alone, K launches back to back on
     # the stream it runs on (the state the stream ended in), bracketed by HIP
@@ -305,8 +312,12 @@ def main():
         "select_commit": {"avg_ms": round(sel_ms, 5), "masked_rows": nmask, "GB_per_s": round(sel_gbs, 1),
                           "masked_rows_per_step_in_stream": float(masked_rows.mean())},
         "tokens_committed_per_step": round(float(nc.sum(1).mean()), 3),
-        # P_c: committed tokens over window slots processed, over the timed steps
-        "P_c": round(float(nc.sum()) / (K * B * W), 4),
+        # P_c = N_new / N_total over the timed steps, from the library's
+        # device counters (committed tokens over window slots processed)
+        "P_c": round(float(cnt[:, 0].sum()) / float(max(cnt[:, 1].sum(), 1)), 4),
+        "counters": {"N_new": int(cnt[:, 0].sum()), "N_total": int(cnt[:, 1].sum()),
+                     "matches_commit_history": bool(int(cnt[:, 0].sum()) == int(nc.sum())
+                                                    and int(cnt[:, 1].sum()) == K * B * W)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args),
                      "kernel": "wedlm_step_attn (attn_split + attn_combine)"},

@@ -64,12 +64,12 @@ def load_library():
     lib.wedlm_step_attn.restype = C.c_int
     lib.wedlm_select_commit_workspace.argtypes = [i32, i32, i32]
     lib.wedlm_select_commit_workspace.restype = sz
-    lib.wedlm_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P,
+    lib.wedlm_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
                                         C.c_float, C.c_float, i32, P, sz, P]
     lib.wedlm_select_commit.restype = C.c_int
     lib.wedlm_lmhead_select_commit_workspace.argtypes = [i32, i32, i32, i32]
     lib.wedlm_lmhead_select_commit_workspace.restype = sz
-    lib.wedlm_lmhead_select_commit.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+    lib.wedlm_lmhead_select_commit.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P,
                                                C.c_float, C.c_float, i32, P, sz, P]
     lib.wedlm_lmhead_select_commit.restype = C.c_int
     lib.wedlm_dual_stream_attn_workspace.argtypes = [S, i32]
@@ -79,8 +79,8 @@ def load_library():
     Mp = C.POINTER(WedlmModel)
     lib.wedlm_model_step_workspace.argtypes = [Mp, S, i32]
     lib.wedlm_model_step_workspace.restype = sz
-    lib.wedlm_model_step.argtypes = [Mp, S, P, P, P, P, P, P, P, P, P, P, C.c_float, C.c_float, C.c_double, i32,
-                                     P, sz, P, P]
+    lib.wedlm_model_step.argtypes = [Mp, S, P, P, P, P, P, P, P, P, P, P, P, C.c_float, C.c_float, C.c_double,
+                                     i32, P, sz, P, P]
     lib.wedlm_model_step.restype = C.c_int
     lib.wedlm_attn_plan.argtypes = [S, i32, C.POINTER(i32), C.POINTER(i32)]
     lib.wedlm_attn_plan.restype = C.c_int
@@ -236,7 +236,9 @@ def select_workspace_tensor(B: int, W: int, V: int, device):
 
 def wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit, committed, alpha: float,
                         tau: float, mask_id: int, workspace, argmax_out=None, entropy_out=None,
-                        stream=None):
+                        counters=None, stream=None):
+    """counters: optional [B, 2] int64 tensor accumulating (N_new, N_total):
+    committed tokens and processed window slots per sequence."""
     import torch
     if logits.dim() != 3 or logits.dtype != torch.float32:
         raise WedlmError("logits must be a [B, W, V] float32 tensor")
@@ -249,13 +251,14 @@ def wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit, committed, 
     _expect(committed, "committed", (B, W), torch.int32)
     _opt(argmax_out, "argmax_out", (B, W), torch.int32)
     _opt(entropy_out, "entropy_out", (B, W), torch.float32)
+    _opt(counters, "counters", (B, 2), torch.int64)
     if workspace is None or workspace.dtype != torch.uint8:
         raise WedlmError("workspace must be a uint8 tensor (select_workspace_tensor)")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().wedlm_select_commit(
         B, W, V, _ptr(logits), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len), _ptr(n_commit),
-        _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), float(alpha), float(tau), int(mask_id),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(counters), float(alpha), float(tau),
+        int(mask_id), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def wedlm_lmhead_select_commit_workspace(B: int, W: int, V: int, Dm: int) -> int:
@@ -273,7 +276,7 @@ def lmhead_workspace_tensor(B: int, W: int, V: int, Dm: int, device):
 
 def wedlm_lmhead_select_commit(hidden, lm_head, tok, filled, pos, ctx_len, n_commit, committed,
                                alpha: float, tau: float, mask_id: int, workspace, argmax_out=None,
-                               entropy_out=None, stream=None):
+                               entropy_out=None, counters=None, stream=None):
     """hidden [B, W, Dm] and lm_head [V, Dm] bfloat16 tensors; window state
     and outputs as for wedlm_select_commit."""
     import torch
@@ -292,13 +295,14 @@ def wedlm_lmhead_select_commit(hidden, lm_head, tok, filled, pos, ctx_len, n_com
     _expect(committed, "committed", (B, W), torch.int32)
     _opt(argmax_out, "argmax_out", (B, W), torch.int32)
     _opt(entropy_out, "entropy_out", (B, W), torch.float32)
+    _opt(counters, "counters", (B, 2), torch.int64)
     if workspace is None or workspace.dtype != torch.uint8:
         raise WedlmError("workspace must be a uint8 tensor (lmhead_workspace_tensor)")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load_library().wedlm_lmhead_select_commit(
         B, W, V, Dm, _ptr(hidden), _ptr(lm_head), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len),
-        _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), float(alpha), float(tau),
-        int(mask_id), _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(counters), float(alpha),
+        float(tau), int(mask_id), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def _dual_shape(qm, km, block):
@@ -381,7 +385,8 @@ def model_step_workspace_tensor(handle: ModelHandle, shape: WedlmShape, max_ctx_
 
 def wedlm_model_step(handle: ModelHandle, shape: WedlmShape, block_table, tok, filled, pos, ctx_len, n_commit,
                      committed, alpha: float, tau: float, rope_base: float, max_ctx_len: int, workspace,
-                     argmax_out=None, entropy_out=None, hidden_out=None, dev_status=None, stream=None):
+                     argmax_out=None, entropy_out=None, hidden_out=None, dev_status=None, counters=None,
+                     stream=None):
     import torch
     B, W = shape.B, shape.W
     _expect(block_table, "block_table", (B, shape.max_pages), torch.int32)
@@ -394,13 +399,14 @@ def wedlm_model_step(handle: ModelHandle, shape: WedlmShape, block_table, tok, f
     _opt(argmax_out, "argmax_out", (B, W), torch.int32)
     _opt(entropy_out, "entropy_out", (B, W), torch.float32)
     _opt(hidden_out, "hidden_out", (B, W, handle.d_model), torch.bfloat16)
+    _opt(counters, "counters", (B, 2), torch.int64)
     _opt(dev_status, "dev_status", (1,), torch.int32)
     if workspace is None or workspace.dtype != torch.uint8:
         raise WedlmError("workspace must be a uint8 tensor (model_step_workspace_tensor)")
     _check(load_library().wedlm_model_step(
         C.byref(handle.model), C.byref(shape), _ptr(block_table), _ptr(tok), _ptr(filled), _ptr(pos),
-        _ptr(ctx_len), _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(hidden_out),
-        float(alpha), float(tau), float(rope_base), int(max_ctx_len), _ptr(workspace),
+        _ptr(ctx_len), _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(counters),
+        _ptr(hidden_out), float(alpha), float(tau), float(rope_base), int(max_ctx_len), _ptr(workspace),
         workspace.numel(), _ptr(dev_status), _stream(stream)))
 
 

@@ -261,8 +261,9 @@ extern "C" size_t wedlm_lmhead_select_commit_workspace(int32_t B, int32_t W, int
 extern "C" int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32_t Dm, const void* hidden,
                                           const void* lm_head, int32_t* tok, uint8_t* filled, int32_t* pos,
                                           int32_t* ctx_len, int32_t* n_commit, int32_t* committed,
-                                          int32_t* argmax_out, float* entropy_out, float alpha, float tau,
-                                          int32_t mask_id, void* workspace, size_t ws_bytes, void* stream) {
+                                          int32_t* argmax_out, float* entropy_out, int64_t* counters, float alpha,
+                                          float tau, int32_t mask_id, void* workspace, size_t ws_bytes,
+                                          void* stream) {
     LmheadLayout L;
     if (!lmhead_layout(B, W, V, Dm, &L))
         return fail(WEDLM_ERR_SHAPE,
@@ -291,6 +292,7 @@ extern "C" int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32
     SelectArgs a;
     a.logits = nullptr; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
     a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;
+    a.counters = counters;
     a.part = g.row_stat;
     a.B = B; a.W = W; a.V = V; a.nparts = 1; a.part_len = V;
     a.alpha = alpha; a.tau = tau; a.mask_id = mask_id;
@@ -359,7 +361,8 @@ extern "C" size_t wedlm_model_step_workspace(const wedlm_model* m, const wedlm_s
 
 extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, const int32_t* block_table, int32_t* tok,
                                 uint8_t* filled, int32_t* pos, int32_t* ctx_len, int32_t* n_commit, int32_t* committed,
-                                int32_t* argmax_out, float* entropy_out, void* hidden_out, float alpha, float tau,
+                                int32_t* argmax_out, float* entropy_out, int64_t* counters, void* hidden_out,
+                                float alpha, float tau,
                                 double rope_base, int32_t max_ctx_len, void* workspace, size_t ws_bytes,
                                 int32_t* dev_status, void* stream) {
     ModelLayout L;
@@ -445,8 +448,8 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
         if (rc) return rc;
     }
     return wedlm_lmhead_select_commit(s->B, s->W, m->vocab, d, ws + L.h, m->lm_head, tok, filled, pos, ctx_len,
-                                      n_commit, committed, argmax_out, entropy_out, alpha, tau, m->vocab, ws + L.lm,
-                                      L.lm_bytes, stream);
+                                      n_commit, committed, argmax_out, entropy_out, counters, alpha, tau, m->vocab,
+                                      ws + L.lm, L.lm_bytes, stream);
 }
 
 extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_t* nsplit, int32_t* split_keys) {
@@ -528,8 +531,9 @@ extern "C" size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V)
 
 extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float* logits, int32_t* tok,
                                    uint8_t* filled, int32_t* pos, int32_t* ctx_len, int32_t* n_commit,
-                                   int32_t* committed, int32_t* argmax_out, float* entropy_out, float alpha,
-                                   float tau, int32_t mask_id, void* workspace, size_t ws_bytes, void* stream) {
+                                   int32_t* committed, int32_t* argmax_out, float* entropy_out, int64_t* counters,
+                                   float alpha, float tau, int32_t mask_id, void* workspace, size_t ws_bytes,
+                                   void* stream) {
     if (B < 1 || W < 1 || W > 64 || V < 1)
         return fail(WEDLM_ERR_SHAPE, "need B >= 1, 1 <= W <= 64, V >= 1 (B=%d W=%d V=%d)", B, W, V);
     if ((int64_t)B * W * ((V + kPartLen - 1) / kPartLen) > (1ll << 30)) return fail(WEDLM_ERR_SHAPE, "grid too large");
@@ -544,6 +548,7 @@ extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float*
     SelectArgs a;
     a.logits = logits; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
     a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;
+    a.counters = counters;
     a.part = static_cast<float4*>(workspace);
     a.B = B; a.W = W; a.V = V; a.nparts = np; a.part_len = pl;
     a.alpha = alpha; a.tau = tau; a.mask_id = mask_id;

@@ -53,6 +53,7 @@ struct SelectArgs {
     int32_t* committed;
     int32_t* argmax_out;
     float* entropy_out;
+    int64_t* counters;    // [B][2] (N_new, N_total) accumulated, or nullptr
     float4* part;         // [B*W][nparts]: (m, argmax bits, S, T)
     int B, W, V, nparts, part_len;
     float alpha, tau;

@@ -154,6 +154,13 @@ __global__ __launch_bounds__(64) void commit_select_refill(SelectArgs a) {
     if (lane == 0) {
         a.n_commit[b] = k;
         a.ctx_len[b] = L + k;
+        // prefix cacheability: N_new counts committed tokens, N_total the
+        // window slots this step processed (one wave per sequence, so the
+        // update needs no atomics)
+        if (a.counters) {
+            a.counters[2 * b] += k;
+            a.counters[2 * b + 1] += W;
+        }
     }
 }
 

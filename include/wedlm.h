@@ -188,20 +188,26 @@ size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V);
  *     fallback and the tie-breaks are this library's reading of the rule.
  *  3. refill: slots shift left by k; k masks (tok = mask_id, filled = 0)
  *     enter at the right; pos[b][i] = ctx_len[b] + i.
+ *  4. counters (if given): counters[b][0] += k (N_new: tokens committed to
+ *     the cached prefix) and counters[b][1] += W (N_total: window slots this
+ *     step ran through the model), so that the prefix cacheability of the
+ *     stream is P_c = N_new / N_total ("Key claims", sec. 3.1, Eq. 4).
  *
  *   logits   [B][W][V] fp32 device (rows of filled slots are not read)
  *   tok, filled, pos [B][W], ctx_len [B]   device, updated in place
  *   n_commit [B], committed [B][W]         device out
  *   argmax_out [B][W] int32, entropy_out [B][W] fp32   device out or NULL;
  *            masked slots get a_j / H_j, filled slots -1 / -1.0f
+ *   counters [B][2] int64 device, accumulated in place (the caller zeroes
+ *            it at the start of a stream), or NULL
  *   workspace / ws_bytes  see wedlm_select_commit_workspace
  * Logits must be finite.  W <= 64, V >= 1.
  */
 int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float *logits, int32_t *tok,
                         uint8_t *filled, int32_t *pos, int32_t *ctx_len, int32_t *n_commit,
                         int32_t *committed, int32_t *argmax_out, float *entropy_out,
-                        float alpha, float tau, int32_t mask_id, void *workspace,
-                        size_t ws_bytes, void *stream);
+                        int64_t *counters, float alpha, float tau, int32_t mask_id,
+                        void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * wedlm_lmhead_select_commit_workspace -- bytes of device workspace for
@@ -239,8 +245,9 @@ size_t wedlm_lmhead_select_commit_workspace(int32_t B, int32_t W, int32_t V, int
 int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32_t Dm, const void *hidden,
                                const void *lm_head, int32_t *tok, uint8_t *filled, int32_t *pos,
                                int32_t *ctx_len, int32_t *n_commit, int32_t *committed,
-                               int32_t *argmax_out, float *entropy_out, float alpha, float tau,
-                               int32_t mask_id, void *workspace, size_t ws_bytes, void *stream);
+                               int32_t *argmax_out, float *entropy_out, int64_t *counters,
+                               float alpha, float tau, int32_t mask_id, void *workspace,
+                               size_t ws_bytes, void *stream);
 
 /*
  * wedlm_dual_stream_attn_workspace -- bytes of device workspace for
@@ -335,7 +342,8 @@ size_t wedlm_model_step_workspace(const wedlm_model *m, const wedlm_shape *s, in
  *            num_pages of the layer caches; dtype WEDLM_BF16
  *   block_table [B][max_pages], shared by every layer's cache
  *   tok, filled, pos, ctx_len, n_commit, committed, argmax_out,
- *   entropy_out, alpha, tau  as for wedlm_select_commit (mask_id = vocab)
+ *   entropy_out, counters, alpha, tau  as for wedlm_select_commit
+ *            (mask_id = vocab)
  *   hidden_out  [B][W][d_model] bf16 device out (the final normalised
  *            hidden states) or NULL
  *   rope_base, max_ctx_len   as for wedlm_reorder / wedlm_step_attn
@@ -344,9 +352,9 @@ size_t wedlm_model_step_workspace(const wedlm_model *m, const wedlm_shape *s, in
  */
 int wedlm_model_step(const wedlm_model *m, const wedlm_shape *s, const int32_t *block_table, int32_t *tok,
                      uint8_t *filled, int32_t *pos, int32_t *ctx_len, int32_t *n_commit, int32_t *committed,
-                     int32_t *argmax_out, float *entropy_out, void *hidden_out, float alpha, float tau,
-                     double rope_base, int32_t max_ctx_len, void *workspace, size_t ws_bytes,
-                     int32_t *dev_status, void *stream);
+                     int32_t *argmax_out, float *entropy_out, int64_t *counters, void *hidden_out,
+                     float alpha, float tau, double rope_base, int32_t max_ctx_len, void *workspace,
+                     size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
  * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for

@@ -174,6 +174,23 @@ def select_commit(logits: np.ndarray, tok, filled, pos, ctx_len, alpha: float, t
                 committed=committed, argmax=am, entropy=ent, margin=margin)
 
 
+def prefix_cacheability(n_commit_steps, W: int):
+    """Prefix cacheability of a stream (paper-summary page, "Key claims",
+    sec. 3.1, Eq. 4: P_c = N_new / N_total, committed tokens over all token
+    positions the decoder ran through; only the former join the cached
+    prefix whose K/V later steps reuse).  Reading:
+    every step processes the W window slots of each sequence (N_total += W)
+    and commits its leading filled run (N_new += n_commit).
+    n_commit_steps: [steps][B] commit counts.  Returns (N_new [B], N_total
+    [B], P_c [B]) with the counts as int64."""
+    n = np.asarray(n_commit_steps, dtype=np.int64)
+    if n.ndim == 1:
+        n = n[None]
+    n_new = n.sum(axis=0)
+    n_total = np.full(n.shape[1], n.shape[0] * int(W), dtype=np.int64)
+    return n_new, n_total, n_new / np.maximum(n_total, 1)
+
+
 def lmhead_logits(hidden: np.ndarray, lm_head: np.ndarray) -> np.ndarray:
     """Logits of the LM head: z[..., v] = sum_k hidden[..., k] * lm_head[v, k]
     in float64 (numpy's matmul as the contraction).  The inputs are the

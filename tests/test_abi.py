@@ -135,16 +135,16 @@ def test_split_override_validation():
 def test_select_commit_validation_and_workspace():
     lib = wd.load_library()
     fake = C.c_void_p(0x1000)
-    assert lib.wedlm_select_commit(0, 16, 100, *([fake] * 9), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_SHAPE
-    assert lib.wedlm_select_commit(2, 65, 100, *([fake] * 9), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_SHAPE
-    assert lib.wedlm_select_commit(2, 16, 100, *([None] * 9), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_ARG
-    assert lib.wedlm_select_commit(2, 16, 100, *([fake] * 9), float("nan"), 1.0, 100, fake, 1 << 20,
+    assert lib.wedlm_select_commit(0, 16, 100, *([fake] * 10), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_SHAPE
+    assert lib.wedlm_select_commit(2, 65, 100, *([fake] * 10), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_SHAPE
+    assert lib.wedlm_select_commit(2, 16, 100, *([None] * 10), 0.1, 1.0, 100, fake, 1 << 20, None) == ERR_ARG
+    assert lib.wedlm_select_commit(2, 16, 100, *([fake] * 10), float("nan"), 1.0, 100, fake, 1 << 20,
                                    None) == ERR_ARG
     need = lib.wedlm_select_commit_workspace(64, 16, 151936)
     assert need >= 64 * 16 * 10 * 16      # one float4 per (slot, 16384 logits)
-    assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 9), 0.1, 1.0, 100, fake, need - 1,
+    assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 10), 0.1, 1.0, 100, fake, need - 1,
                                    None) == ERR_WS
-    assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 9), 0.1, 1.0, 100, None, need, None) == ERR_WS
+    assert lib.wedlm_select_commit(64, 16, 151936, *([fake] * 10), 0.1, 1.0, 100, None, need, None) == ERR_WS
 
 
 def test_binding_refuses_host_tensors():
@@ -197,14 +197,14 @@ def test_lmhead_validation_and_workspace():
     for bad in [(0, 16, 100, 64), (1, 65, 100, 64), (65, 64, 100, 64), (1, 8, 0, 64), (1, 8, 100, 96),
                 (1, 8, 100, 0), (1, 8, 100, 65536 + 64)]:
         assert ws(*bad) == 0, bad
-    args = [fake] * 10 + [C.c_float(0.1), C.c_float(1.0), 100, fake, C.c_size_t(1 << 30), None]
+    args = [fake] * 11 + [C.c_float(0.1), C.c_float(1.0), 100, fake, C.c_size_t(1 << 30), None]
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 96, *args) == ERR_SHAPE
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, None, *args[1:]) == ERR_ARG
     misaligned = C.c_void_p(0x1008)
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, misaligned, *args[1:]) == ERR_ARG
-    small = args[:14] + [C.c_size_t(ws(1, 8, 100, 64) - 1), None]
+    small = args[:15] + [C.c_size_t(ws(1, 8, 100, 64) - 1), None]
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, *small) == ERR_WS
-    nan = args[:10] + [C.c_float(float("nan"))] + args[11:]
+    nan = args[:11] + [C.c_float(float("nan"))] + args[12:]
     assert lib.wedlm_lmhead_select_commit(1, 8, 100, 64, *nan) == ERR_ARG
 
 
@@ -220,3 +220,44 @@ def test_dual_stream_validation():
                                       None) == ERR_ARG
     need = lib.wedlm_dual_stream_attn_workspace(C.byref(ok), 256)
     assert lib.wedlm_dual_stream_attn(C.byref(ok), 256, *([fake] * 9), 1e6, fake, need - 1, None, None) == ERR_WS
+
+
+def _model_struct(d_model=256, d_ff=512, vocab=1000, addr=0x1000, misaligned_field=None):
+    from causal_attention_diffusion_amd.binding import LAYER_FIELDS, WedlmLayerWeights, WedlmModel
+    vals = [addr + 0x100000 * i for i in range(len(LAYER_FIELDS))]
+    if misaligned_field is not None:
+        vals[LAYER_FIELDS.index(misaligned_field)] += 8
+    layers = (WedlmLayerWeights * 1)(WedlmLayerWeights(*vals))
+    m = WedlmModel(1, d_model, d_ff, vocab, 1e-6, addr + 0x2000000, addr + 0x3000000, addr + 0x4000000,
+                   C.cast(layers, C.POINTER(WedlmLayerWeights)))
+    return m, layers
+
+
+def test_model_step_validation_and_workspace():
+    """Shape, pointer, alignment and workspace checks of wedlm_model_step
+    (all fail before any launch)."""
+    lib = wd.load_library()
+    fake = C.c_void_p(0x1000)
+    shape = wd.make_shape(2, 8, 4, 2, 64, 8, 16, wd.WEDLM_BF16)   # d_model = Hq * D = 256
+    m, keep = _model_struct()
+    need = lib.wedlm_model_step_workspace(C.byref(m), C.byref(shape), 64)
+    assert need > 0
+    bad_d, keep2 = _model_struct(d_model=512)                         # != Hq * D
+    assert lib.wedlm_model_step_workspace(C.byref(bad_d), C.byref(shape), 64) == 0
+    bad_ff, keep3 = _model_struct(d_ff=300)                           # not a multiple of 256
+    assert lib.wedlm_model_step_workspace(C.byref(bad_ff), C.byref(shape), 64) == 0
+
+    def call(model, ptrs=None, ws=fake, ws_bytes=None):
+        p = [fake] * 7 if ptrs is None else ptrs   # block_table .. committed
+        return lib.wedlm_model_step(C.byref(model), C.byref(shape), *p, None, None, None, None, C.c_float(0.25),
+                                    C.c_float(2.0), C.c_double(1e4), 64, ws,
+                                    C.c_size_t(need if ws_bytes is None else ws_bytes), None, None)
+
+    assert call(bad_d) == ERR_SHAPE
+    assert call(m, ptrs=[None] + [fake] * 6) == ERR_ARG
+    for f in ("wq", "w_down", "attn_norm"):
+        mis, keep4 = _model_struct(misaligned_field=f)
+        assert call(mis) == ERR_ARG, f
+    assert call(m, ws=None) == ERR_WS
+    assert call(m, ws_bytes=need - 1) == ERR_WS
+    assert "workspace" in wd.wedlm_last_error()

@@ -76,6 +76,8 @@ def _run_stream(cfg, dev, steps, max_ctx):
     tok, filled, pos, ctx = wl.initial_window(B, W, cfg.vocab)
     caches = [([np.zeros((0, cfg.Hkv, cfg.D))] * B, [np.zeros((0, cfg.Hkv, cfg.D))] * B) for _ in range(cfg.layers)]
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    counters = torch.zeros((B, 2), dtype=torch.int64, device=dev)
+    commits = []
     worst = 0.0
     for step in range(steps):
         st = [torch.from_numpy(np.ascontiguousarray(x, dt)).to(dev)
@@ -86,7 +88,7 @@ def _run_stream(cfg, dev, steps, max_ctx):
         ent = torch.empty((B, W), dtype=torch.float32, device=dev)
         hid = torch.empty((B, W, cfg.d_model), dtype=torch.bfloat16, device=dev)
         wd.wedlm_model_step(handle, shape, bt_t, *st, n_commit, committed, cfg.alpha, cfg.tau, cfg.rope_base, max_ctx,
-                            ws, argmax_out=am, entropy_out=ent, hidden_out=hid, dev_status=status)
+                            ws, argmax_out=am, entropy_out=ent, hidden_out=hid, dev_status=status, counters=counters)
         torch.cuda.synchronize()
         assert status.item() == 0
         ref = oracle.model_step(w64, caches, tok, filled, pos, ctx, cfg.alpha, cfg.tau, cfg.rope_base, cfg.eps,
@@ -115,6 +117,9 @@ def _run_stream(cfg, dev, steps, max_ctx):
                 ties += 1
         assert (sel["margin"] > 1e-4).all(), sel["margin"]
         np.testing.assert_array_equal(n_commit.cpu().numpy(), sel["n_commit"])
+        commits.append(sel["n_commit"])
+        n_new, n_total, _ = oracle.prefix_cacheability(commits, W)
+        np.testing.assert_array_equal(counters.cpu().numpy(), np.stack([n_new, n_total], axis=1))
         np.testing.assert_array_equal(st[3].cpu().numpy(), sel["ctx_len"])
         if ties == 0:
             np.testing.assert_array_equal(st[0].cpu().numpy(), sel["tok"])

@@ -312,7 +312,7 @@ def _state_to_dev(tok, filled, pos, ctx, dev):
             torch.from_numpy(np.ascontiguousarray(ctx, np.int32)).to(dev))
 
 
-def _gpu_select(logits, st, alpha, tau, mask_id, ws):
+def _gpu_select(logits, st, alpha, tau, mask_id, ws, counters=None):
     tok, filled, pos, ctx = st
     B, W, V = logits.shape
     dev = logits.device
@@ -321,7 +321,7 @@ def _gpu_select(logits, st, alpha, tau, mask_id, ws):
     am = torch.empty((B, W), dtype=torch.int32, device=dev)
     ent = torch.empty((B, W), dtype=torch.float32, device=dev)
     wd.wedlm_select_commit(logits, tok, filled, pos, ctx, n_commit, committed, alpha, tau, mask_id, ws,
-                           argmax_out=am, entropy_out=ent)
+                           argmax_out=am, entropy_out=ent, counters=counters)
     return n_commit, committed, am, ent
 
 
@@ -365,12 +365,16 @@ def test_select_stream_small_free_running(B, W, V, dev):
     ws = wd.select_workspace_tensor(B, W, V, dev)
     tok, filled, pos, ctx = wl.initial_window(B, W, V)
     st = _state_to_dev(tok, filled, pos, ctx, dev)
+    # prefix-cacheability counters (N_new, N_total) accumulate on the device
+    counters = torch.zeros((B, 2), dtype=torch.int64, device=dev)
+    hist = []
     for step in range(cfg.steps):
         lg = wl.make_logits_np(cfg, step)
         if V < 16:
             lg[..., 0] += 3.0
         ref = oracle.select_commit(lg, tok, filled, pos, ctx, cfg.alpha, cfg.tau, V)
-        outs = _gpu_select(torch.from_numpy(lg).to(dev), st, cfg.alpha, cfg.tau, V, ws)
+        hist.append(ref["n_commit"])
+        outs = _gpu_select(torch.from_numpy(lg).to(dev), st, cfg.alpha, cfg.tau, V, ws, counters=counters)
         torch.cuda.synchronize()
         if V > 1:
             _check_step(ref, st, outs)
@@ -378,6 +382,8 @@ def test_select_stream_small_free_running(B, W, V, dev):
             np.testing.assert_array_equal(st[0].cpu().numpy(), ref["tok"])
             np.testing.assert_array_equal(st[1].cpu().numpy(), ref["filled"])
         tok, filled, pos, ctx = ref["tok"], ref["filled"], ref["pos"], ref["ctx_len"]
+    n_new, n_total, _ = oracle.prefix_cacheability(hist, W)
+    np.testing.assert_array_equal(counters.cpu().numpy(), np.stack([n_new, n_total], axis=1))
 
 
 def test_select_window_full_commits_all(dev):
