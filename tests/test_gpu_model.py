@@ -146,3 +146,15 @@ def test_model_qwen3_layer_one_step(dev):
     # on a 4 x 64 window: 256 rows, split-K projections, two row tiles
     cfg = wl.MODEL_CONFIGS["model_qwen3_layer"]
     _run_stream(cfg, dev, 1, max_ctx=cfg.W)
+
+
+@pytest.mark.parametrize("B,W", [(3, 48), (5, 64), (9, 64)])
+def test_model_ragged_row_counts(B, W, dev):
+    # window row counts that end inside a 32-row MFMA tile and inside a
+    # 256-row group (144 = 128 + 16; 320 and 576 need two and three row
+    # groups in every projection and in the LM head)
+    import dataclasses
+    cfg = dataclasses.replace(wl.MODEL_CONFIGS["model_small"], name=f"model_b{B}w{W}", B=B, W=W, layers=1,
+                              seed=1600 + B * W, steps=3)
+    ctx = _run_stream(cfg, dev, cfg.steps, max_ctx=cfg.steps * cfg.W)
+    assert (ctx >= 0).all()
