@@ -17,8 +17,9 @@ tokens in 16-token pages (shuffled), window 32 (16 observed), bf16; logits
 Prints one JSON line (rank 0).  Three timed regions: (1) K whole streaming
 steps, bracketed by device synchronisation, give ms_per_step and the
 headline window tokens/s: launched eagerly (reported as eager_ms_per_step),
-then, unless --eager, the same K steps captured once as a HIP graph and
-replayed from the same starting state, as a serving loop would run them
+then, unless --eager, the same K steps captured once as a HIP graph with the
+library's own capture API (wedlm_graph_begin / end / launch) and replayed
+from the same starting state, as a serving loop would run them
 (this replay gives ms_per_step and the value); (2) K back-to-back launches of the attention call
 on the final state, bracketed by HIP events on its stream, give the mean
 launch time the roofline divides the launch's algorithmic bytes (K/V of
@@ -44,6 +45,7 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long_b4.md")
 ATTN_SOURCES = ["attn_bf16.hip", "attn.hip", "api.hip", "kernels.hpp", "common.hpp"]
 METRIC = "window tokens/sec and decode steps/sec per GPU; attn achieved HBM GB/s vs peak"
+ATTN_SETTLE = 100   # untimed attention launches before the roofline leg
 
 
 def parse():
@@ -73,6 +75,20 @@ def parse():
                     help="only run a plain device copy of MIB MiB (5 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+def capture_steps(fn):
+    """Record the library calls fn() makes as one HIP graph with the
+    library's own capture API (wedlm_graph_begin / end), on a side stream
+    ordered after the current one; replay with .launch()."""
+    import torch
+    import causal_attention_diffusion_amd as wd
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with wd.capture(cap) as g:
+        fn()
+    torch.cuda.current_stream().wait_stream(cap)
+    return g
 
 
 def copy_calibration(mib):
@@ -185,33 +201,35 @@ def main():
     eager_elapsed = time.perf_counter() - t0
     elapsed = eager_elapsed
     if not args.eager:
+        state_eager = [x.clone() for x in (tok, filled, pos, ctx, counters)]
         for x, y in zip((tok, filled, pos, ctx), state0):
             x.copy_(y)
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(args.warmup, total_steps):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(cap)
+        graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total_steps)])
         for _ in range(2):
             for x, y in zip((tok, filled, pos, ctx), state0):
                 x.copy_(y)
             counters.zero_()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            graph.replay()
+            graph.launch()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - t0
+        for x, y in zip((tok, filled, pos, ctx, counters), state_eager):
+            if not torch.equal(x, y):
+                print("graph replay diverged from the eager steps", file=sys.stderr)
+                sys.exit(3)
     cnt = counters.cpu().numpy()
 
     # ---- timed region 2: the attention call alone, K launches back to back on
     # the stream it runs on (the state the stream ended in), bracketed by HIP
     # events on that stream: its mean launch duration for the roofline.
+    # The first launches of a process run slower while the board settles
+    # (up to 140 us instead of about 105 us at long_b4), so the leg starts
+    # after ATTN_SETTLE untimed launches of the same call.
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    attention()
+    for _ in range(ATTN_SETTLE):
+        attention()
     ev0.record(stream)
     for _ in range(args.steps):
         attention()
@@ -378,19 +396,12 @@ def bench_select(args):
     elapsed = eager_elapsed
     if not args.eager:
         reset()
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(args.warmup, total):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(cap)
+        graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total)])
         for _ in range(2):
             reset()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            graph.replay()
+            graph.launch()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx), state_eager):
@@ -480,19 +491,12 @@ def bench_lmhead(args):
     elapsed = eager_elapsed
     if not args.eager:
         reset()
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(args.warmup, total):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(cap)
+        graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total)])
         for _ in range(2):
             reset()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            graph.replay()
+            graph.launch()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx), state_eager):
@@ -681,19 +685,12 @@ def bench_model(args):
     elapsed = eager_elapsed
     if not args.eager:
         reset()
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(graph, stream=cap):
-                for i in range(args.warmup, total):
-                    step(i)
-        torch.cuda.current_stream().wait_stream(cap)
+        graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total)])
         for _ in range(2):
             reset()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            graph.replay()
+            graph.launch()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx), state_eager):

@@ -16,6 +16,8 @@ if the library is not built, every call raises.
 from .binding import (  # noqa: F401
     WEDLM_BF16,
     WEDLM_F32,
+    Graph,
+    capture,
     WedlmError,
     attn_plan,
     lib_path,

@@ -86,6 +86,16 @@ def load_library():
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
     lib.wedlm_set_attn_split_keys.restype = C.c_int
+    lib.wedlm_graph_begin.argtypes = [P]
+    lib.wedlm_graph_begin.restype = C.c_int
+    lib.wedlm_graph_end.argtypes = [P, C.POINTER(C.c_void_p)]
+    lib.wedlm_graph_end.restype = C.c_int
+    lib.wedlm_graph_launch.argtypes = [P, P]
+    lib.wedlm_graph_launch.restype = C.c_int
+    lib.wedlm_graph_nodes.argtypes = [P, C.POINTER(sz), C.POINTER(sz)]
+    lib.wedlm_graph_nodes.restype = C.c_int
+    lib.wedlm_graph_destroy.argtypes = [P]
+    lib.wedlm_graph_destroy.restype = None
     lib.wedlm_last_error.restype = C.c_char_p
     lib.wedlm_version.restype = C.c_char_p
     _LIB = lib
@@ -416,3 +426,65 @@ def wedlm_last_error() -> str:
 
 def wedlm_version() -> str:
     return load_library().wedlm_version().decode()
+
+
+class Graph:
+    """A captured sequence of library calls (wedlm_graph_*), replayed with
+    launch().  Made by capture(); destroyed with close() or when collected."""
+
+    def __init__(self):
+        self._h = C.c_void_p()
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise WedlmError("graph is empty or closed")
+        _check(load_library().wedlm_graph_launch(self._h, _stream(stream)))
+
+    def nodes(self):
+        """(kernel nodes, other nodes) of the captured graph."""
+        k, o = C.c_size_t(), C.c_size_t()
+        _check(load_library().wedlm_graph_nodes(self._h, C.byref(k), C.byref(o)))
+        return k.value, o.value
+
+    def close(self):
+        if self._h:
+            load_library().wedlm_graph_destroy(self._h)
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class capture:
+    """Record the library calls made inside the block on `stream` (a
+    torch.cuda.Stream other than the default one) into a Graph:
+
+        with wd.capture(side_stream) as g:
+            step(...)            # recorded, not run
+        g.launch()               # replays every recorded call
+
+    Inside the block `stream` is torch's current stream, so the calls need
+    no stream argument.  Nothing that allocates may run inside the block."""
+
+    def __init__(self, stream):
+        import torch
+        if stream is None or stream.cuda_stream == 0:
+            raise WedlmError("capture needs a created stream, not the default stream")
+        self.stream = stream
+        self.graph = Graph()
+        self._ctx = torch.cuda.stream(stream)
+
+    def __enter__(self):
+        _check(load_library().wedlm_graph_begin(self.stream.cuda_stream))
+        self._ctx.__enter__()
+        return self.graph
+
+    def __exit__(self, exc_type, exc, tb):
+        self._ctx.__exit__(exc_type, exc, tb)
+        rc = load_library().wedlm_graph_end(self.stream.cuda_stream, C.byref(self.graph._h))
+        if exc_type is None:
+            _check(rc)
+        return False

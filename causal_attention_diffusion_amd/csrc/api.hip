@@ -555,6 +555,65 @@ extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float*
     return hip_status(launch_select(a, (hipStream_t)stream), "wedlm_select_commit launch");
 }
 
+// ---------------------------------------------------------------- graph capture
+struct wedlm_graph {
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+extern "C" int wedlm_graph_begin(void* stream) {
+    if (!stream) return fail(WEDLM_ERR_ARG, "graph capture needs a created stream, not the default stream");
+    return hip_status(hipStreamBeginCapture((hipStream_t)stream, hipStreamCaptureModeThreadLocal),
+                      "wedlm_graph_begin");
+}
+
+extern "C" int wedlm_graph_end(void* stream, wedlm_graph** out) {
+    if (!stream || !out) return fail(WEDLM_ERR_ARG, "wedlm_graph_end: NULL stream or output");
+    *out = nullptr;
+    hipGraph_t g = nullptr;
+    int rc = hip_status(hipStreamEndCapture((hipStream_t)stream, &g), "wedlm_graph_end capture");
+    if (rc) return rc;
+    hipGraphExec_t e = nullptr;
+    rc = hip_status(hipGraphInstantiate(&e, g, nullptr, nullptr, 0), "wedlm_graph_end instantiate");
+    if (rc) {
+        (void)hipGraphDestroy(g);
+        return rc;
+    }
+    *out = new wedlm_graph{g, e};
+    g_err[0] = 0;
+    return WEDLM_OK;
+}
+
+extern "C" int wedlm_graph_launch(const wedlm_graph* g, void* stream) {
+    if (!g) return fail(WEDLM_ERR_ARG, "wedlm_graph_launch: NULL graph");
+    return hip_status(hipGraphLaunch(g->exec, (hipStream_t)stream), "wedlm_graph_launch");
+}
+
+extern "C" int wedlm_graph_nodes(const wedlm_graph* g, size_t* kernels, size_t* others) {
+    if (!g || !kernels || !others) return fail(WEDLM_ERR_ARG, "wedlm_graph_nodes: NULL argument");
+    size_t n = 0;
+    int rc = hip_status(hipGraphGetNodes(g->graph, nullptr, &n), "wedlm_graph_nodes");
+    if (rc) return rc;
+    *kernels = *others = 0;
+    if (n == 0) return WEDLM_OK;
+    hipGraphNode_t* nodes = new hipGraphNode_t[n];
+    rc = hip_status(hipGraphGetNodes(g->graph, nodes, &n), "wedlm_graph_nodes");
+    for (size_t i = 0; rc == WEDLM_OK && i < n; ++i) {
+        hipGraphNodeType t;
+        rc = hip_status(hipGraphNodeGetType(nodes[i], &t), "wedlm_graph_nodes");
+        if (rc == WEDLM_OK) ++(t == hipGraphNodeTypeKernel ? *kernels : *others);
+    }
+    delete[] nodes;
+    return rc;
+}
+
+extern "C" void wedlm_graph_destroy(wedlm_graph* g) {
+    if (!g) return;
+    (void)hipGraphExecDestroy(g->exec);
+    (void)hipGraphDestroy(g->graph);
+    delete g;
+}
+
 extern "C" const char* wedlm_last_error(void) { return g_err; }
 
 extern "C" const char* wedlm_version(void) { return "wedlm-mi355x 0.1 (gfx950)"; }

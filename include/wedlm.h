@@ -371,6 +371,37 @@ int wedlm_attn_plan(const wedlm_shape *s, int32_t max_ctx_len, int32_t *nsplit,
  */
 int wedlm_set_attn_split_keys(int32_t keys);
 
+/*
+ * Graph capture of decode steps -- the launch-latency remedy the pages
+ * point to for a small causal prefill over the window ("Key claims",
+ * sec. 5.2: the step stays a standard causal forward, so graph capture
+ * applies unchanged).  Every entry point above only launches kernels and
+ * device copies on its stream -- no allocation, no synchronisation, no
+ * memset -- so any sequence of them (for example K whole steps of
+ * reorder, attention and select) can be recorded once and replayed as one
+ * launch:
+ *
+ *   wedlm_graph_begin(stream);            stream: a created stream, not 0
+ *   ... library calls on `stream` ...     recorded, not run
+ *   wedlm_graph_end(stream, &g);          instantiates; *g owned by caller
+ *   wedlm_graph_launch(g, stream2);       replays on any stream, any times
+ *   wedlm_graph_destroy(g);
+ *
+ * A replay reads and writes the buffers the recorded calls named, with the
+ * scalars (shapes, alpha, tau, ...) fixed at capture; the caller restores
+ * or advances the window state between replays as the recorded steps
+ * expect.  Capture is thread-local (hipStreamCaptureModeThreadLocal).  If a
+ * call fails validation during capture, call wedlm_graph_end anyway and
+ * destroy what it returns.
+ */
+typedef struct wedlm_graph wedlm_graph;
+int wedlm_graph_begin(void *stream);
+int wedlm_graph_end(void *stream, wedlm_graph **out);
+int wedlm_graph_launch(const wedlm_graph *g, void *stream);
+/* Nodes of a captured graph: kernel launches, and all others (copies). */
+int wedlm_graph_nodes(const wedlm_graph *g, size_t *kernels, size_t *others);
+void wedlm_graph_destroy(wedlm_graph *g);
+
 /* Thread-local message describing the last non-OK status ("" if none). */
 const char *wedlm_last_error(void);
 

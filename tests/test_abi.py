@@ -261,3 +261,18 @@ def test_model_step_validation_and_workspace():
     assert call(m, ws=None) == ERR_WS
     assert call(m, ws_bytes=need - 1) == ERR_WS
     assert "workspace" in wd.wedlm_last_error()
+
+
+def test_graph_api_validation():
+    """The capture entry points reject NULL streams and graphs before any
+    HIP call; destroy(NULL) is a no-op."""
+    lib = wd.load_library()
+    assert lib.wedlm_graph_begin(None) == ERR_ARG
+    out = C.c_void_p()
+    assert lib.wedlm_graph_end(None, C.byref(out)) == ERR_ARG
+    assert lib.wedlm_graph_end(C.c_void_p(0x1000), None) == ERR_ARG
+    assert lib.wedlm_graph_launch(None, None) == ERR_ARG
+    k, o = C.c_size_t(), C.c_size_t()
+    assert lib.wedlm_graph_nodes(None, C.byref(k), C.byref(o)) == ERR_ARG
+    lib.wedlm_graph_destroy(None)
+    assert "NULL" in wd.wedlm_last_error()
