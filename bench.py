@@ -20,11 +20,15 @@ headline window tokens/s: launched eagerly (reported as eager_ms_per_step),
 then, unless --eager, the same K steps captured once as a HIP graph with the
 library's own capture API (wedlm_graph_begin / end / launch) and replayed
 from the same starting state, as a serving loop would run them
-(this replay gives ms_per_step and the value); (2) K back-to-back launches of the attention call
-on the final state, bracketed by HIP events on its stream, give the mean
-launch time the roofline divides the launch's algorithmic bytes (K/V of
-every visible key read once, Q in, O out) by; (3) the select/commit call
-alone, for its own bandwidth.
+(this replay gives ms_per_step and the value); (2) K back-to-back launches
+of the attention call on the final state, bracketed by HIP events on its
+stream, give the mean launch time the roofline divides the launch's
+algorithmic bytes (K/V of every visible key read once, Q in, O out) by; (3)
+the select/commit call alone, for its own bandwidth.  Before each timed
+sequence the same sequence runs untimed from the same starting state for at
+least SETTLE_S seconds (and the attention call ATTN_SETTLE times before its
+leg), because the board reaches steady clocks only after some tenths of a
+second of load.
 """
 import argparse
 import json
@@ -46,6 +50,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long_b4.md")
 ATTN_SOURCES = ["attn_bf16.hip", "attn.hip", "api.hip", "kernels.hpp", "common.hpp"]
 METRIC = "window tokens/sec and decode steps/sec per GPU; attn achieved HBM GB/s vs peak"
 ATTN_SETTLE = 100   # untimed attention launches before the roofline leg
+SETTLE_S = 0.25     # seconds of untimed repeats of the timed sequence before it is timed
 
 
 def parse():
@@ -75,6 +80,22 @@ def parse():
                     help="only run a plain device copy of MIB MiB (5 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+def settle(run, restart, seconds=SETTLE_S):
+    """Run the timed sequence untimed, from its starting state each time,
+    for at least `seconds`: the board only reaches its steady clocks after
+    some tenths of a second of load (the first launches of a process, or
+    the first after an idle gap such as a graph capture, run up to 30 %
+    slower)."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while True:
+        restart()
+        run()
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            break
 
 
 def capture_steps(fn):
@@ -192,28 +213,34 @@ def main():
     # untimed and once timed.  Capture records without running; a replay from
     # the same state rewrites the same cache rows with the same bytes.
     state0 = [x.clone() for x in (tok, filled, pos, ctx)]
-    counters.zero_()
+    def restart():
+        for x, y in zip((tok, filled, pos, ctx), state0):
+            x.copy_(y)
+        counters.zero_()
+
+    def eager_steps():
+        for i in range(args.warmup, total_steps):
+            step(i)
+
+    settle(eager_steps, restart)
+    restart()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, total_steps):
-        step(i)
+    eager_steps()
     torch.cuda.synchronize()
     eager_elapsed = time.perf_counter() - t0
     elapsed = eager_elapsed
     if not args.eager:
         state_eager = [x.clone() for x in (tok, filled, pos, ctx, counters)]
-        for x, y in zip((tok, filled, pos, ctx), state0):
-            x.copy_(y)
-        graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total_steps)])
-        for _ in range(2):
-            for x, y in zip((tok, filled, pos, ctx), state0):
-                x.copy_(y)
-            counters.zero_()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graph.launch()
-            torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t0
+        restart()
+        graph = capture_steps(eager_steps)
+        settle(graph.launch, restart)
+        restart()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.launch()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx, counters), state_eager):
             if not torch.equal(x, y):
                 print("graph replay diverged from the eager steps", file=sys.stderr)
@@ -221,11 +248,11 @@ def main():
     cnt = counters.cpu().numpy()
 
     # ---- timed region 2: the attention call alone, K launches back to back on
-    # the stream it runs on (the state the stream ended in), bracketed by HIP
-    # events on that stream: its mean launch duration for the roofline.
-    # The first launches of a process run slower while the board settles
-    # (up to 140 us instead of about 105 us at long_b4), so the leg starts
-    # after ATTN_SETTLE untimed launches of the same call.
+    # the stream it runs on (the state the stream ended in), bracketed by one
+    # pair of HIP events on that stream: its mean launch duration for the
+    # roofline.  ATTN_SETTLE untimed launches of the same call come first.
+    # (An event pair around every single call inside the steps would add
+    # about 8 us of marker overhead to each measured call.)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(ATTN_SETTLE):
@@ -380,6 +407,7 @@ def bench_select(args):
         step(i)
     # timed: K steps from the all-masked start, eagerly (HIP events on the
     # stream bracket exactly the K calls), then replayed as one HIP graph
+    settle(lambda: [step(i) for i in range(args.warmup, total)], reset)
     reset()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -397,13 +425,13 @@ def bench_select(args):
     if not args.eager:
         reset()
         graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total)])
-        for _ in range(2):
-            reset()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graph.launch()
-            torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t0
+        settle(graph.launch, reset)
+        reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.launch()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx), state_eager):
             if not torch.equal(x, y):
                 print("graph replay diverged from the eager steps", file=sys.stderr)
@@ -475,6 +503,7 @@ def bench_lmhead(args):
 
     for i in range(args.warmup):
         step(i)
+    settle(lambda: [step(i) for i in range(args.warmup, total)], reset)
     reset()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -492,13 +521,13 @@ def bench_lmhead(args):
     if not args.eager:
         reset()
         graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total)])
-        for _ in range(2):
-            reset()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graph.launch()
-            torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t0
+        settle(graph.launch, reset)
+        reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.launch()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx), state_eager):
             if not torch.equal(x, y):
                 print("graph replay diverged from the eager steps", file=sys.stderr)
@@ -570,6 +599,7 @@ def bench_dual(args):
 
     for _ in range(args.warmup):
         step()
+    settle(lambda: [step() for _ in range(args.steps)], lambda: None)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -665,6 +695,7 @@ def bench_model(args):
 
     for i in range(args.warmup):
         step(i)
+    settle(lambda: [step(i) for i in range(args.warmup, total)], reset)
     reset()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -686,13 +717,13 @@ def bench_model(args):
     if not args.eager:
         reset()
         graph = capture_steps(lambda: [step(i) for i in range(args.warmup, total)])
-        for _ in range(2):
-            reset()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            graph.launch()
-            torch.cuda.synchronize()
-            elapsed = time.perf_counter() - t0
+        settle(graph.launch, reset)
+        reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.launch()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx), state_eager):
             if not torch.equal(x, y):
                 print("graph replay diverged from the eager steps", file=sys.stderr)
