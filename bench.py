@@ -780,8 +780,8 @@ def cpu_baseline_model(cfg, w_dev, bt):
     """The oracle's model step, untuned, on the host cores, for the first
     sequence of the first step (64 masked rows after the 2048-token prompt),
     on the bench's own bf16 weights and caches copied to the host.  It runs
-    with the first layer, then the first two; the 36-layer step time is
-    t(2) + 34 (t(2) - t(1))."""
+    with the first layer, then the first four; the 36-layer step time is
+    t(4) + 32 (t(4) - t(1)) / 3."""
     import oracle
     import workloads as wl
 
@@ -795,7 +795,7 @@ def cpu_baseline_model(cfg, w_dev, bt):
     import torch
     t = torch.arange(L0, device=bt.device)
     pg = bt[0].long()[t // 16], t % 16
-    for l in range(2):
+    for l in range(4):
         lw = w_dev["layers"][l]
         layers.append({k: host(v) for k, v in lw.items() if k not in ("k_cache", "v_cache")})
         kc = lw["k_cache"][pg[0], :, pg[1], :]
@@ -803,7 +803,7 @@ def cpu_baseline_model(cfg, w_dev, bt):
         caches.append(([host(kc)], [host(vc)]))
     tok, filled, pos, ctx = wl.initial_window(1, W, cfg.vocab, L0)
     times = {}
-    for n in (1, 2):
+    for n in (1, 4):
         wn = dict(top, layers=layers[:n])
         best = None
         for _ in range(2):
@@ -813,11 +813,12 @@ def cpu_baseline_model(cfg, w_dev, bt):
             dt = time.perf_counter() - t0
             best = dt if best is None else min(best, dt)
         times[n] = best
-    est = times[2] + (cfg.layers - 2) * max(times[2] - times[1], 0.0)
+    per_layer = max(times[4] - times[1], 0.0) / 3
+    est = times[4] + (cfg.layers - 4) * per_layer
     return {"value": round(W / est, 3), "unit": "window tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"sequence 0 of the first step ({W} masked rows, {L0}-token prompt) with 1 and 2 layers "
-                      f"({times[1]:.2f} s, {times[2]:.2f} s, best of 2); {cfg.layers}-layer step estimated as "
-                      f"t2 + {cfg.layers - 2} (t2 - t1) = {est:.2f} s"}
+            "sample": f"sequence 0 of the first step ({W} masked rows, {L0}-token prompt) with 1 and 4 layers "
+                      f"({times[1]:.2f} s, {times[4]:.2f} s, best of 2); {cfg.layers}-layer step estimated as "
+                      f"t4 + {cfg.layers - 4} (t4 - t1) / 3 = {est:.2f} s"}
 
 
 def cpu_baseline_dual(args, arrs, flags, b):
