@@ -174,12 +174,26 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     // split-major order: every (sequence, KV head, row tile) gets its first
     // split dispatched before any second split, so the dispatcher hands the
     // remaining (equal-size) splits of long sequences to whichever CU frees
-    // up first
-    const int npid = a.B * a.Hkv * a.row_tiles;
-    const int split = blockIdx.x / npid;
-    const int pid = blockIdx.x - split * npid;
-    const int rt = pid % a.row_tiles;
-    const int bk = pid / a.row_tiles;
+    // up first.  With several row tiles (W x G > 128 query rows) the row
+    // tiles of one (sequence, KV head, split) stream the same K/V: they take
+    // work-group ids 8 apart, which the dispatcher hands to the same XCD one
+    // after the other, so the later tiles read that K/V from the XCD's L2
+    // (the grid is padded to whole groups of 8; the padding returns at once).
+    const int nbk = a.B * a.Hkv;
+    int split, bk, rt;
+    if (a.row_tiles == 1) {
+        split = blockIdx.x / nbk;
+        bk = blockIdx.x - split * nbk;
+        rt = 0;
+    } else {
+        const int j = blockIdx.x >> 3;
+        rt = j % a.row_tiles;
+        const int q = (j / a.row_tiles) * 8 + (blockIdx.x & 7);
+        split = q / nbk;
+        bk = q - split * nbk;
+        if (split >= a.nsplit) return;
+    }
+    const int pid = bk * a.row_tiles + rt;
     const int kvh = bk % a.Hkv;
     const int b = bk / a.Hkv;
 
@@ -560,10 +574,18 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     }
 }
 
+// Work-groups of the split kernel: one per (sequence, KV head, row tile,
+// split); with several row tiles the (sequence, KV head, split) groups are
+// padded to a multiple of 8 (see the id mapping in the kernel).
+static unsigned bf16_split_grid(const AttnArgs& a) {
+    const long groups = (long)a.B * a.Hkv * a.nsplit;
+    if (a.row_tiles == 1) return (unsigned)groups;
+    return (unsigned)((groups + 7) / 8 * 8 * a.row_tiles);
+}
+
 template <int D, int NRG>
 static hipError_t launch_bf16_t(const AttnArgs& a, hipStream_t st) {
-    const int npid = a.B * a.Hkv * a.row_tiles;
-    hipLaunchKernelGGL((attn_split_bf16<D, NRG>), dim3((unsigned)npid * a.nsplit), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_split_bf16<D, NRG>), dim3(bf16_split_grid(a)), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
