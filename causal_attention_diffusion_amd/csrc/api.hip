@@ -2,6 +2,7 @@
 // launch planning and kernel launches.  No call allocates device memory or
 // synchronises the device.
 #include <math.h>
+#include <new>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -393,10 +394,11 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
     // y = X W^T over up to three weight matrices stacked along the output
     // dimension (rows [0, n1) of W0, [n1, n2) of W1, [n2, N) of W2)
     auto gemm = [&](const void* W0, const void* W1, const void* W2, int n1, int n2, const bf16_t* X, int N, int K,
-                    int S) {
-        GemmArgs g{cbf(W0), cbf(W1), cbf(W2), n1, n2, X, f32(L.P), M, N, K, S, 1};
+                    int S, bf16_t* act = nullptr) {
+        GemmArgs g{cbf(W0), cbf(W1), cbf(W2), n1, n2, X, f32(L.P), M, N, K, S, 1, act};
         return hip_status(launch_gemm(g, st), "wedlm_model_step gemm");
     };
+    const bool swiglu_fused = gemm_swiglu_fused(M, L.Sgu);
     auto rows = [&](bf16_t* out, int N, int S, const void* norm) {
         ModelRowArgs r{};
         r.x_res = f32(L.x_res); r.h = out; r.g = cbf(norm); r.P = f32(L.P);
@@ -432,11 +434,16 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
         if ((rc = gemm(w.wo, w.wo, w.wo, d, d, bf(L.o), d, HqD, L.So))) return rc;
         if ((rc = hip_status(launch_add_rmsnorm(rows(bf(L.h), d, L.So, w.mlp_norm), st), "wedlm_model_step norm")))
             return rc;
-        // act = silu(h Wg^T) * (h Wu^T): one launch over [Wg; Wu]
-        if ((rc = gemm(w.w_gate, w.w_up, w.w_up, F, 2 * F, bf(L.h), 2 * F, d, L.Sgu))) return rc;
-        if ((rc = hip_status(launch_finish_swiglu(rows(bf(L.act), 2 * F, L.Sgu, nullptr), st),
-                             "wedlm_model_step finish")))
-            return rc;
+        // act = silu(h Wg^T) * (h Wu^T): one launch over [Wg; Wu]; with one
+        // K split the launch writes act itself, otherwise a finish sums splits
+        if (swiglu_fused) {
+            if ((rc = gemm(w.w_gate, w.w_up, w.w_up, F, 2 * F, bf(L.h), 2 * F, d, 1, bf(L.act)))) return rc;
+        } else {
+            if ((rc = gemm(w.w_gate, w.w_up, w.w_up, F, 2 * F, bf(L.h), 2 * F, d, L.Sgu))) return rc;
+            if ((rc = hip_status(launch_finish_swiglu(rows(bf(L.act), 2 * F, L.Sgu, nullptr), st),
+                                 "wedlm_model_step finish")))
+                return rc;
+        }
         // x += act Wd^T; h = RMSNorm(x) * next norm
         if ((rc = gemm(w.w_down, w.w_down, w.w_down, d, d, bf(L.act), d, F, L.Sd))) return rc;
         if ((rc = hip_status(launch_add_rmsnorm(rows(bf(L.h), d, L.Sd, next_norm), st), "wedlm_model_step norm")))
@@ -579,7 +586,13 @@ extern "C" int wedlm_graph_end(void* stream, wedlm_graph** out) {
         (void)hipGraphDestroy(g);
         return rc;
     }
-    *out = new wedlm_graph{g, e};
+    wedlm_graph* w = new (std::nothrow) wedlm_graph{g, e};
+    if (!w) {
+        (void)hipGraphExecDestroy(e);
+        (void)hipGraphDestroy(g);
+        return fail(WEDLM_ERR_ARG, "wedlm_graph_end: out of host memory");
+    }
+    *out = w;
     g_err[0] = 0;
     return WEDLM_OK;
 }
@@ -596,7 +609,8 @@ extern "C" int wedlm_graph_nodes(const wedlm_graph* g, size_t* kernels, size_t* 
     if (rc) return rc;
     *kernels = *others = 0;
     if (n == 0) return WEDLM_OK;
-    hipGraphNode_t* nodes = new hipGraphNode_t[n];
+    hipGraphNode_t* nodes = new (std::nothrow) hipGraphNode_t[n];
+    if (!nodes) return fail(WEDLM_ERR_ARG, "wedlm_graph_nodes: out of host memory");
     rc = hip_status(hipGraphGetNodes(g->graph, nodes, &n), "wedlm_graph_nodes");
     for (size_t i = 0; rc == WEDLM_OK && i < n; ++i) {
         hipGraphNodeType t;

@@ -115,7 +115,12 @@ struct GemmArgs {
     const bf16_t* X;        // [M][K]
     float* P;               // [S][M][N] partial products
     int M, N, K, S, nrg;    // nrg set by the launcher
+    // SwiGLU form (act != nullptr): W0 = gate [N/2][K], W1 = up [N/2][K],
+    // S == 1, more than 128 rows; the launch writes act[m][c] =
+    // bf16(silu(gate . x_m) * (up . x_m)) for c < N/2 instead of partials
+    bf16_t* act;
 };
+bool gemm_swiglu_fused(int M, int S);
 int gemm_splits(int M, int N, int K);
 hipError_t launch_gemm(GemmArgs a, hipStream_t stream);
 hipError_t launch_embed_rmsnorm(const ModelRowArgs& a, hipStream_t stream);

@@ -82,7 +82,7 @@ struct StackedRows {
 };
 
 template <class C, class ARows>
-__device__ __forceinline__ void tile_mma_rows(const ARows& arows, int n0, int n_lim, const char* Bm, const int* s_rows,
+__device__ __forceinline__ void tile_mma_rows(const ARows arows, int n0, int n_lim, const char* Bm, const int* s_rows,
                                          int K, int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM]) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -93,8 +93,9 @@ __device__ __forceinline__ void tile_mma_rows(const ARows& arows, int n0, int n_
     // DMA sources of this lane: instruction q of a stage loads RPI row slices
     // (A rows for q < NT/RPI, then B rows); the lane that fills LDS chunk
     // (row, p) reads global chunk swz(row, p).
+    // (the LDS offset of instruction q is q KB either way: the A rows fill
+    // the first ABYTES = NT/RPI KB of a slot, the B rows follow)
     const char* gsrc[C::LPS];
-    uint32_t ldst[C::LPS];
 #pragma unroll
     for (int u = 0; u < C::LPS; ++u) {
         const int q = w * C::LPS + u;
@@ -103,20 +104,19 @@ __device__ __forceinline__ void tile_mma_rows(const ARows& arows, int n0, int n_
             const int row = q * C::RPI + lane / C::CPR;
             const int n = min(n0 + row, n_lim - 1);
             gsrc[u] = arows(n) + C::swz(row, p) * 16;
-            ldst[u] = q * 1024;
         } else {
             const int m = (q - C::NT / C::RPI) * C::RPI + lane / C::CPR;
             gsrc[u] = Bm + (size_t)s_rows[m] * rowbytes + C::swz(m, p) * 16;
-            ldst[u] = C::ABYTES + (q - C::NT / C::RPI) * 1024;
         }
     }
+    static_assert(C::ABYTES == C::NT / C::RPI * 1024, "A rows fill whole 1 KB loads");
     auto issue = [&](int st) {
-        char* slot = s_ring + (st % C::SLOTS) * C::SLOTB;
+        char* slot = s_ring + (st % C::SLOTS) * C::SLOTB + w * C::LPS * 1024;
 #pragma unroll
         for (int u = 0; u < C::LPS; ++u)
             __builtin_amdgcn_global_load_lds(
                 (const void*)(gsrc[u] + (size_t)st * C::RB),
-                (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(slot + ldst[u])), 16, 0, 0);
+                (__attribute__((address_space(3))) void*)(reinterpret_cast<uintptr_t>(slot + u * 1024)), 16, 0, 0);
     };
 
     const int wn = w % C::WN, wm = w / C::WN;

@@ -160,8 +160,75 @@ __global__ __launch_bounds__(256) void finish_swiglu(ModelRowArgs a) {
     }
 }
 
+// Gate and up rows interleaved by tiles of 128: rows [0, 64) of tile t are
+// gate rows 64t .. 64t+63, rows [64, 128) the up rows of the same outputs,
+// so one work-group holds both factors of every SwiGLU output it owns.
+struct PairedRows {
+    const char* gate;
+    const char* up;
+    size_t rowbytes;
+    __device__ const char* operator()(int n) const {
+        // arithmetic choice of the base (a conditional between the two
+        // members would become a dynamically indexed field load and keep
+        // the functor in memory)
+        const int r = n & 127;
+        const uintptr_t g = reinterpret_cast<uintptr_t>(gate), u = reinterpret_cast<uintptr_t>(up);
+        const uintptr_t base = g + (uintptr_t)(r >> 6) * (u - g);
+        return reinterpret_cast<const char*>(base) + (size_t)((n >> 7) * 64 + (r & 63)) * rowbytes;
+    }
+};
+
+// The SwiGLU epilogue of one 128 x 256 tile (WN = 2): the waves holding the
+// up rows (wave_n 1) pass their accumulators through LDS to the waves
+// holding the gate rows of the same outputs (wave_n 0), which write
+// act[m][c] = bf16(silu(g) * u) -- a lane's 16 values of one 32-row block
+// are 4 runs of 4 consecutive outputs.
+template <class C>
+__device__ __forceinline__ void swiglu_epilogue(const GemmArgs& a, int m0, int tile, char* s_ring,
+                                                const f32x16 (&acc)[C::TN][C::TM]) {
+    static_assert(C::NT == 128 && C::WN == 2 && C::TN == 2, "paired tile shape");
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wn = C::wave_n(), wm = C::wave_m();
+    const int hl = lane >> 5, col = lane & 31;
+    float* s_up = reinterpret_cast<float*>(s_ring);    // [wm][x][y][e][lane]
+    tile_block_sync();                                   // every wave is done with the ring
+    if (wn == 1) {
+#pragma unroll
+        for (int x = 0; x < C::TN; ++x)
+#pragma unroll
+            for (int y = 0; y < C::TM; ++y)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    s_up[(((wm * C::TN + x) * C::TM + y) * 16 + e) * 64 + lane] = acc[x][y][e];
+    }
+    __syncthreads();
+    if (wn != 0) return;
+    const int F = a.N / 2;
+#pragma unroll
+    for (int y = 0; y < C::TM; ++y) {
+        const int m = m0 + (wm * C::TM + y) * 32 + col;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int x = 0; x < C::TN; ++x)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int c = tile * 64 + x * 32 + g4 * 8 + hl * 4;
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * g4 + i;
+                    const float u = s_up[(((wm * C::TN + x) * C::TM + y) * 16 + e) * 64 + lane];
+                    v[i] = silu(acc[x][y][e]) * u;
+                }
+                if (c < F)
+                    *reinterpret_cast<uint2*>(a.act + (size_t)m * F + c) = pack_bf16x4(make_float4(v[0], v[1], v[2], v[3]));
+            }
+    }
+}
+
 // P[s][m][n] = sum over the s-th K range of X[m][k] W[n][k], fp32, W the
-// stacked weight rows.  Work-group i: split s = i % S (so the work-groups of
+// stacked weight rows (or, in the SwiGLU form, the activation directly).  Work-group i: split s = i % S (so the work-groups of
 // one K range share an XCD when S divides 8 or 8 divides S), then row
 // group, then output tile.
 template <class C>
@@ -179,9 +246,18 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
     __syncthreads();
     const int kr = a.K / a.S;
     const size_t k0b = (size_t)s * kr * 2;
+    f32x16 acc[C::TN][C::TM];
+    if constexpr (C::NT == 128 && C::WN == 2 && C::TN == 2) {
+        if (a.act) {
+            const PairedRows rows{reinterpret_cast<const char*>(a.W0), reinterpret_cast<const char*>(a.W1),
+                                  (size_t)a.K * 2};
+            tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X), s_rows, a.K, a.K, s_ring, acc);
+            swiglu_epilogue<C>(a, m0, nt, s_ring, acc);
+            return;
+        }
+    }
     const StackedRows rows{reinterpret_cast<const char*>(a.W0) + k0b, reinterpret_cast<const char*>(a.W1) + k0b,
                            reinterpret_cast<const char*>(a.W2) + k0b, a.n1, a.n2, (size_t)a.K * 2};
-    f32x16 acc[C::TN][C::TM];
     tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X) + k0b, s_rows, kr, a.K, s_ring, acc);
     const int wn = C::wave_n(), wm = C::wave_m();
     const int hl = lane >> 5, col = lane & 31;
@@ -222,7 +298,11 @@ int gemm_splits(int M, int N, int K) {
     return S;
 }
 
+// The SwiGLU form runs on the 256-row tile with a single K split.
+bool gemm_swiglu_fused(int M, int S) { return M > GemmSmall::MT && S == 1; }
+
 hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
+    if (a.act && !gemm_swiglu_fused(a.M, a.S)) return hipErrorInvalidValue;
     if (a.M <= GemmSmall::MT) {
         a.nrg = 1;
         const unsigned g = (unsigned)(((a.N + GemmSmall::NT - 1) / GemmSmall::NT) * a.S);
