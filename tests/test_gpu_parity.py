@@ -233,6 +233,49 @@ def test_edge_cases(label, over, split, dev):
         wd.wedlm_set_attn_split_keys(0)
 
 
+def _random_shapes(n, seed):
+    """Seeded draws over the shapes the entry points accept: batch, window
+    (1..64), head grouping (G = 1..8), head dim, dtype, ragged prefixes
+    (some empty), observed counts and split-size overrides."""
+    rng = np.random.default_rng(seed)
+    heads = [(8, 8), (8, 2), (16, 4), (32, 8), (32, 4), (64, 8), (4, 2)]
+    out = []
+    for i in range(n):
+        hq, hkv = heads[int(rng.integers(len(heads)))]
+        dtype = "f32" if rng.random() < 0.3 else "bf16"
+        D = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 5))
+        W = int(rng.integers(1, 65))
+        lo = int(rng.integers(0, 300))
+        L_range = (lo, lo + int(rng.integers(0, 400)))
+        split = int(rng.choice([0, 0, 64, 128, 320]))
+        over = dict(B=B, W=W, Hq=hq, Hkv=hkv, D=D, dtype=dtype, L=0, L_range=L_range, n_obs=None,
+                    seed=9000 + i, positions=("contiguous",), rope_base=1e4 if dtype == "f32" else 1e6)
+        out.append((f"r{i}_B{B}W{W}G{hq // hkv}D{D}_{dtype}_s{split}", over, split))
+    return out
+
+
+@pytest.mark.parametrize("label,over,split", _random_shapes(24, 2027), ids=lambda v: v if isinstance(v, str) else "")
+def test_random_shapes_reorder_attention(label, over, split, dev):
+    # whole reorder + attention against the oracle on seeded random shapes
+    cfg = _cfg("qwen3_l2048", name=label, **over)
+    print(f"[random] {label}", flush=True)
+    wd.wedlm_set_attn_split_keys(split)
+    try:
+        inp = wl.make_attn_inputs(cfg)
+        t = wl.device_attn_inputs(inp, dev)
+        run_reorder(t, cfg)
+        run_attn(t, int(inp.ctx_len.max()))
+        torch.cuda.synchronize()
+        assert t["status"].item() == 0
+        ref = oracle.decode_step_attention(inp)
+        np.testing.assert_array_equal(t["perm"].cpu().numpy(), ref["perm"])
+        err = rel_err(wl.torch_storage_to_f64(t["out"], cfg.dtype), ref["out"])
+        assert err <= ATTN_TOL[cfg.dtype], err
+    finally:
+        wd.wedlm_set_attn_split_keys(0)
+
+
 def test_split_count_does_not_change_result(dev):
     cfg = wl.CONFIGS["qwen3_l2048"]
     outs = []
