@@ -2,6 +2,7 @@
 // launch planning and kernel launches.  No call allocates device memory or
 // synchronises the device.
 #include <math.h>
+#include <atomic>
 #include <new>
 #include <stdarg.h>
 #include <stdio.h>
@@ -77,19 +78,19 @@ extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const 
 }
 
 // ---------------------------------------------------------------- attention plan
-static int32_t g_split_override = 0;
+static std::atomic<int32_t> g_split_override{0};   // process-wide, read by every plan
 
 // Compute units of the current device (cached per device; 256 on MI355X).
 static int device_cus() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];   // 0 = not queried yet; threads may race to fill a slot
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 static const int64_t kMaxContext = 524288;  // keys incl. the window (at most 64 splits)
 
@@ -109,8 +110,9 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     const int64_t T = (int64_t)max_ctx_len + s->W;
     const int64_t pairs = (int64_t)s->B * s->Hkv * p.row_tiles;
     int64_t sk;
-    if (g_split_override > 0) {
-        sk = g_split_override;
+    const int32_t override_keys = g_split_override.load(std::memory_order_relaxed);
+    if (override_keys > 0) {
+        sk = override_keys;
     } else {
         // One round of work-groups over the device (a bf16 work-group fills a
         // CU's LDS): the key work of every (sequence, KV head, row tile) at
@@ -474,7 +476,7 @@ extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_
 extern "C" int wedlm_set_attn_split_keys(int32_t keys) {
     if (keys != 0 && (keys < 64 || keys > kMaxSplitPages * kPage || keys % 64 != 0))
         return fail(WEDLM_ERR_ARG, "split keys must be 0 or a multiple of 64 in [64, %d]", kMaxSplitPages * kPage);
-    g_split_override = keys;
+    g_split_override.store(keys, std::memory_order_relaxed);
     g_err[0] = 0;
     return WEDLM_OK;
 }
