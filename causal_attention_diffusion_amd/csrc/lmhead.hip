@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * C::NW) void lmhead_stats(LmheadArgs a) {
     const int hl = lane >> 5, col = lane & 31;
     f32x16 acc[C::TN][C::TM];
     tile_mma<C>(reinterpret_cast<const char*>(a.lm_head), n0, a.V, reinterpret_cast<const char*>(a.hidden), s_rows,
-                a.Dm, a.Dm, s_ring, acc);
+                a.Dm, a.Dm, s_ring, acc, cnt - c0);
 
     // ---- statistics of this tile per hidden row
     tile_block_sync();   // every wave is done with the ring

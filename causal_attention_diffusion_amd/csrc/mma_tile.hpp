@@ -57,7 +57,8 @@ __device__ __forceinline__ void tile_block_sync() {
 // rows ld elements long (arows(n) and B point at the first element of the
 // K range of their row).  A rows at or past n_lim repeat row n_lim - 1 (the
 // caller ignores their results); B rows are s_rows[0 .. MT) (LDS, set and
-// synchronised by the caller).  s_ring: C::SLOTS * C::SLOTB bytes of LDS.
+// synchronised by the caller), of which the first m_valid matter: a wave
+// whose B rows all lie past them leaves its acc at zero.  s_ring: C::SLOTS * C::SLOTB bytes of LDS.
 // Ends with a barrier-free ring: the caller synchronises before reusing
 // s_ring.
 // A row addresses: row n of a single matrix of `rowbytes`-long rows.
@@ -83,7 +84,8 @@ struct StackedRows {
 
 template <class C, class ARows>
 __device__ __forceinline__ void tile_mma_rows(const ARows arows, int n0, int n_lim, const char* Bm, const int* s_rows,
-                                         int K, int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM]) {
+                                         int K, int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM],
+                                         int m_valid = C::MT) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,8 +135,27 @@ __device__ __forceinline__ void tile_mma_rows(const ARows arows, int n0, int n_l
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
 
+    // A wave whose B rows all lie at or past m_valid (a partly used row
+    // group) only loads and synchronises: its results would be discarded,
+    // and leaving the MFMA pipe to the other wave of its SIMD speeds that one
+    // up.  The flag is wave-uniform.
+    const bool active = wm * C::TM * 32 < m_valid;
     const int npro = ns < C::AHEAD ? ns : C::AHEAD;
     for (int st = 0; st < npro; ++st) issue(st);
+    if (!active) {
+        // the same waits, barriers and loads as the compute loop below
+        for (int st = 0; st < ns; ++st) {
+            switch (min(C::AHEAD - 1, ns - 1 - st)) {
+                case 3: tile_wait_vm<3 * C::LPS>(); break;
+                case 2: tile_wait_vm<2 * C::LPS>(); break;
+                case 1: tile_wait_vm<C::LPS>(); break;
+                default: tile_wait_vm<0>(); break;
+            }
+            tile_block_sync();
+            if (st + C::AHEAD < ns) issue(st + C::AHEAD);
+        }
+        return;
+    }
     for (int st = 0; st < ns; ++st) {
         // this wave's loads of stage st have landed (up to AHEAD-1 later
         // stages may still be in flight); the barrier publishes every wave's
@@ -170,8 +191,8 @@ __device__ __forceinline__ void tile_mma_rows(const ARows arows, int n0, int n_l
 // The same over a single A matrix.
 template <class C>
 __device__ __forceinline__ void tile_mma(const char* A, int n0, int n_lim, const char* Bm, const int* s_rows, int K,
-                                         int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM]) {
-    tile_mma_rows<C>(PlainRows{A, (size_t)ld * 2}, n0, n_lim, Bm, s_rows, K, ld, s_ring, acc);
+                                         int ld, char* s_ring, f32x16 (&acc)[C::TN][C::TM], int m_valid = C::MT) {
+    tile_mma_rows<C>(PlainRows{A, (size_t)ld * 2}, n0, n_lim, Bm, s_rows, K, ld, s_ring, acc, m_valid);
 }
 
 }  // namespace wedlm

@@ -251,14 +251,15 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
         if (a.act) {
             const PairedRows rows{reinterpret_cast<const char*>(a.W0), reinterpret_cast<const char*>(a.W1),
                                   (size_t)a.K * 2};
-            tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X), s_rows, a.K, a.K, s_ring, acc);
+            tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X), s_rows, a.K, a.K, s_ring, acc,
+                             a.M - m0);
             swiglu_epilogue<C>(a, m0, nt, s_ring, acc);
             return;
         }
     }
     const StackedRows rows{reinterpret_cast<const char*>(a.W0) + k0b, reinterpret_cast<const char*>(a.W1) + k0b,
                            reinterpret_cast<const char*>(a.W2) + k0b, a.n1, a.n2, (size_t)a.K * 2};
-    tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X) + k0b, s_rows, kr, a.K, s_ring, acc);
+    tile_mma_rows<C>(rows, n0, a.N, reinterpret_cast<const char*>(a.X) + k0b, s_rows, kr, a.K, s_ring, acc, a.M - m0);
     const int wn = C::wave_n(), wm = C::wave_m();
     const int hl = lane >> 5, col = lane & 31;
     float* P = a.P + (size_t)s * a.M * a.N;
