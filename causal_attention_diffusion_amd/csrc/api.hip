@@ -20,7 +20,7 @@ void set_error(const char* fmt, ...) {
     va_end(ap);
 }
 
-static int fail(int code, const char* fmt, ...) {
+__attribute__((format(printf, 2, 3))) static int fail(int code, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
@@ -465,7 +465,8 @@ extern "C" int wedlm_attn_plan(const wedlm_shape* s, int32_t max_ctx_len, int32_
     int rc = check_shape(s);
     if (rc) return rc;
     if (max_ctx_len < 0) return fail(WEDLM_ERR_ARG, "max_ctx_len must be >= 0");
-    if ((int64_t)max_ctx_len + s->W > kMaxContext) return fail(WEDLM_ERR_UNSUPPORTED, "context beyond %d tokens", kMaxContext);
+    if ((int64_t)max_ctx_len + s->W > kMaxContext)
+        return fail(WEDLM_ERR_UNSUPPORTED, "context beyond %lld tokens", (long long)kMaxContext);
     Plan p = make_plan(s, max_ctx_len);
     if (nsplit) *nsplit = p.nsplit;
     if (split_keys) *split_keys = p.split_keys;
@@ -497,8 +498,8 @@ extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const v
     if (max_ctx_len < 0 || (int64_t)max_ctx_len + s->W > (int64_t)s->max_pages * kPage)
         return fail(WEDLM_ERR_SHAPE, "max_ctx_len %d + W exceeds max_pages * page_size", max_ctx_len);
     if ((int64_t)max_ctx_len + s->W > kMaxContext)
-        return fail(WEDLM_ERR_UNSUPPORTED, "context of %d tokens: built for up to %d (64 splits of 8192 keys)",
-                    max_ctx_len + s->W, kMaxContext);
+        return fail(WEDLM_ERR_UNSUPPORTED, "context of %lld tokens: built for up to %lld (64 splits of 8192 keys)",
+                    (long long)max_ctx_len + s->W, (long long)kMaxContext);
     if (!(scale >= 0.f) || !isfinite(scale)) return fail(WEDLM_ERR_ARG, "scale must be finite and >= 0");
     Plan p = make_plan(s, max_ctx_len);
     if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes))

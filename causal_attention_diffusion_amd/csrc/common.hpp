@@ -57,5 +57,5 @@ __device__ __forceinline__ void set_status(int32_t* st, uint32_t bit) {
 
 // Host-side helpers (defined in api.hip).
 namespace wedlm {
-void set_error(const char* fmt, ...);
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
 }  // namespace wedlm

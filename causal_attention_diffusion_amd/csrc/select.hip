@@ -36,7 +36,6 @@ __global__ __launch_bounds__(256) void vocab_stats(SelectArgs a) {
     const int wv = tid >> 6;
     const int row = blockIdx.x / a.nparts;  // b * W + j
     const int part = blockIdx.x - row * a.nparts;
-    const int b = row / a.W;
 
     __shared__ Stat s_red[4];
 
