@@ -276,3 +276,24 @@ def test_graph_api_validation():
     assert lib.wedlm_graph_nodes(None, C.byref(k), C.byref(o)) == ERR_ARG
     lib.wedlm_graph_destroy(None)
     assert "NULL" in wd.wedlm_last_error()
+
+
+def test_missing_library_fails_loudly():
+    """Without libwedlm.so every entry point raises: there is no fallback
+    path (a fresh interpreter, with the binding pointed at a path that does
+    not exist)."""
+    code = (
+        "import causal_attention_diffusion_amd.binding as b\n"
+        "b._LIB = None\n"
+        "b._LIB_PATH = '/nonexistent/libwedlm.so'\n"
+        "import causal_attention_diffusion_amd as wd\n"
+        "for f in (lambda: b.load_library(), lambda: wd.wedlm_version()):\n"
+        "    try:\n"
+        "        f()\n"
+        "    except b.WedlmError as e:\n"
+        "        assert 'not built' in str(e) and 'no fallback' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('no error raised')\n"
+        "print('raised')\n")
+    r = subprocess.run(["python3", "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
