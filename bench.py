@@ -134,8 +134,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding paragraph of DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (the path would "
+              "shard by sequence and KV head, or by key range with one all-gather of the split "
+              "partials; that is a design, not code)", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "select_v152k":
