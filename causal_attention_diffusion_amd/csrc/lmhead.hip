@@ -31,10 +31,11 @@
 
 namespace wedlm {
 
-// up to 128 window rows: the weights stream once, HBM-bound
-using LmSmall = TileCfg<256, kLmMT, 64, 3, 4>;
-// more rows: 256-row groups, waves of 128 x 64 (8 MFMAs per fragment set)
-using LmLarge = TileCfg<256, 2 * kLmMT, 32, 4, 2>;
+// 256 vocabulary entries x 128 masked rows per work-group, waves of 64 x 64,
+// K in stages of 64 (whole 128-byte lines of every row).  A 256 x 256 tile
+// in stages of 32 moves fewer bytes per flop but fetches each line in two
+// halves, and measured slower at every window size tried.
+using LmTile = TileCfg<256, kLmMT, 64, 3, 4>;
 
 // Compact list of the masked rows (global row b*W + j, increasing) and
 // their count.  One work-group; a thread owns a contiguous run of rows.
@@ -166,15 +167,9 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned nvt8 = (unsigned)((a.nvt + 7) / 8);
-    if (a.R <= LmSmall::MT) {
-        LmheadArgs b = a;
-        b.nrg = 1;
-        hipLaunchKernelGGL(lmhead_stats<LmSmall>, dim3(8u * nvt8), dim3(64 * LmSmall::NW), 0, st, b);
-    } else {
-        LmheadArgs b = a;
-        b.nrg = (a.R + LmLarge::MT - 1) / LmLarge::MT;
-        hipLaunchKernelGGL(lmhead_stats<LmLarge>, dim3(8u * nvt8 * (unsigned)b.nrg), dim3(64 * LmLarge::NW), 0, st, b);
-    }
+    LmheadArgs b = a;
+    b.nrg = (a.R + LmTile::MT - 1) / LmTile::MT;
+    hipLaunchKernelGGL(lmhead_stats<LmTile>, dim3(8u * nvt8 * (unsigned)b.nrg), dim3(64 * LmTile::NW), 0, st, b);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_merge, dim3((unsigned)a.R), dim3(64), 0, st, a);
