@@ -75,14 +75,20 @@ __global__ __launch_bounds__(64 * C::NW) void lmhead_stats(LmheadArgs a) {
     // Work-groups are handed to the 8 XCDs in turn.  The row groups of one
     // vocabulary tile get consecutive ids on the same XCD, so the tile's
     // weights come from HBM once and from that XCD's L2 for the others.
+    // Only the row groups that hold masked rows take ids (the count is
+    // device state; the grid is sized for every row): the active groups of a
+    // tile are consecutive and the unused ids come last.  Interleaving the
+    // unused ids with the active ones let the tiles' work-groups drift apart
+    // in time, and a weight line lives in L2 for only microseconds here.
     const int i = blockIdx.x;
     const int xcd = i & 7, j = i >> 3;
-    const int rg = j % a.nrg;
-    const int vt = (j / a.nrg) * 8 + xcd;
-    if (vt >= a.nvt) return;
     const int cnt = *a.count;
+    const int na = min(a.nrg, (cnt + C::MT - 1) / C::MT);   // row groups with masked rows
+    if (na <= 0) return;
+    const int rg = j % na;
+    const int vt = (j / na) * 8 + xcd;
+    if (vt >= a.nvt) return;
     const int c0 = rg * C::MT;
-    if (c0 >= cnt) return;
     if (tid < C::MT) s_rows[tid] = a.rows[min(c0 + tid, cnt - 1)];   // rows past the count repeat a valid one
     __syncthreads();
     const int n0 = vt * C::NT;
