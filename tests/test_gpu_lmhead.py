@@ -136,6 +136,20 @@ def test_lmhead_partly_filled_window(dev):
     _stream(cfg, dev, cfg.steps, filled_pattern=pat)
 
 
+@pytest.mark.parametrize("n_masked", [1, 127, 128, 129, 300, 512, 640, 700, 896, 1023])
+def test_lmhead_masked_counts(n_masked, dev):
+    """A 64 x 16 window (room for 8 row groups of 128) with n_masked masked
+    slots scattered over it: every count of active row groups from 1 to 8,
+    with full and partly filled last groups, maps each masked row to exactly
+    one work-group per vocabulary tile (12 tiles, the last one 184 wide)."""
+    B, W, V = 64, 16, 3000
+    cfg = wl.LmheadConfig(f"m{n_masked}", B=B, W=W, Dm=256, V=V, seed=1400 + n_masked, alpha=0.25,
+                          tau=float(np.log(V) * 0.8), steps=1)
+    pat = np.ones(B * W, np.uint8)
+    pat[np.random.default_rng(n_masked).choice(B * W, n_masked, replace=False)] = 0
+    _stream(cfg, dev, 1, filled_pattern=pat.reshape(B, W))
+
+
 def test_lmhead_no_masked_slot(dev):
     # nothing to score: commit the whole window, refill, no kernel reads
     cfg = wl.LmheadConfig("n", B=2, W=8, Dm=64, V=300, seed=1302, alpha=0.25, tau=1.0, steps=1)
