@@ -179,6 +179,10 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     // work-group ids 8 apart, which the dispatcher hands to the same XCD one
     // after the other, so the later tiles read that K/V from the XCD's L2
     // (the grid is padded to whole groups of 8; the padding returns at once).
+    // Inside a split, sequences take ids from the last to the first: where a
+    // batch lists its windows by increasing length (the Dual-Stream layout
+    // lists each sequence's windows so), the longest are dispatched first
+    // and the short ones fill the tail.
     const int nbk = a.B * a.Hkv;
     int split, bk, rt;
     if (a.row_tiles == 1) {
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         bk = q - split * nbk;
         if (split >= a.nsplit) return;
     }
+    bk = nbk - 1 - bk;
     const int pid = bk * a.row_tiles + rt;
     const int kvh = bk % a.Hkv;
     const int b = bk / a.Hkv;
