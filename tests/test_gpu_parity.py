@@ -200,6 +200,10 @@ EDGE = [
     ("G1_D64", dict(B=2, W=16, L=77, n_obs=5, Hq=8, Hkv=8, D=64, dtype="bf16"), 0),
     ("G8", dict(B=2, W=16, L=129, n_obs=7, Hq=32, Hkv=4, dtype="bf16"), 0),
     ("W64_G8_rowtiles4", dict(B=1, W=64, L=200, n_obs=31, Hq=64, Hkv=8, dtype="bf16"), 0),
+    # the largest head grouping the header admits: 1024 query rows per KV head
+    ("W64_G16_rowtiles8", dict(B=2, W=64, L=150, n_obs=20, Hq=64, Hkv=4, dtype="bf16"), 0),
+    ("f32_W64_G16_D64", dict(B=1, W=64, L=90, n_obs=40, Hq=32, Hkv=2, D=64, dtype="f32",
+                             positions=("contiguous",)), 0),
     ("ragged_tails_split64", dict(B=6, W=16, L_range=(1, 200), n_obs=None, dtype="bf16"), 64),
     ("ragged_tails_split128", dict(B=6, W=16, L_range=(1, 200), n_obs=None, dtype="bf16"), 128),
     ("f32_D128_split64", dict(B=2, W=8, L=150, n_obs=3, Hq=8, Hkv=2, D=128, dtype="f32",
