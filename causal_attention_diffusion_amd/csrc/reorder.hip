@@ -42,8 +42,10 @@ __device__ __forceinline__ void store4(bf16_t* p, const float (&x)[4]) {
     *reinterpret_cast<uint2*>(p) = v;
 }
 
+constexpr int kReorderThreads = 512;
+
 template <typename T>
-__global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
+__global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderArgs a) {
     const int i = blockIdx.x;   // logical slot
     const int b = blockIdx.y;
     const int W = a.W, D = a.D, half = D / 2;
@@ -63,11 +65,11 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
     // kMaxItems items per thread is loaded before the permutation, the page
     // and the angle table are known.  (Plain code, no lambdas: arrays
     // captured by a lambda were kept in scratch memory by the compiler.)
-    constexpr int kMaxItems = 4;
+    constexpr int kMaxItems = 2;
     float x0[kMaxItems][4], x1[kMaxItems][4];
 #pragma unroll
     for (int u = 0; u < kMaxItems; ++u) {
-        const int it = tid + u * 256;
+        const int it = tid + u * kReorderThreads;
         if (it >= n_all) continue;
         if (it < qn + kn) {
             const bool isq = it < qn;
@@ -135,11 +137,11 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
     __syncthreads();
 
     // Every later batch loads all its items before using any.
-    for (int base = tid; base < n_all; base += kMaxItems * 256) {
+    for (int base = tid; base < n_all; base += kMaxItems * kReorderThreads) {
         if (base != tid)   // the first batch is already loaded
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * 256;
+            const int it = base + u * kReorderThreads;
             if (it >= n_all) continue;
             if (it < qn + kn) {
                 const bool isq = it < qn;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * 256;
+            const int it = base + u * kReorderThreads;
             if (it >= n_all || (it >= qn && page < 0)) continue;   // no cache row without a page
             if (it < qn + kn) {
                 const bool isq = it < qn;
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void reorder_rope_append(ReorderArgs a) {
 }
 
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream) {
-    dim3 grid(a.W, a.B), block(256);
+    dim3 grid(a.W, a.B), block(kReorderThreads);
     if (dtype == WEDLM_F32)
         hipLaunchKernelGGL(reorder_rope_append<float>, grid, block, 0, stream, a);
     else
