@@ -42,6 +42,34 @@ __device__ __forceinline__ void store4(bf16_t* p, const float (&x)[4]) {
     *reinterpret_cast<uint2*>(p) = v;
 }
 
+// float64 -> bf16 in one rounding (nearest, ties to even).  Normal range:
+// round the double's 52-bit fraction to bf16's 7 bits on the integer
+// pattern; the result has 8 significant bits, so the conversion to fp32 is
+// exact (or overflows to inf, as the rounding demands) and its upper half
+// is the bf16 pattern.  Below 2^-126 bf16 is subnormal with the fixed
+// quantum 2^-133: x * 2^133 is rounded to an integer instead.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+    if (x != x) return 0x7fc0;
+    if (fabs(x) < 0x1p-126) {
+        const double r = rint(x * 0x1p133) * 0x1p-133;
+        return static_cast<uint16_t>(__float_as_uint(static_cast<float>(r)) >> 16);
+    }
+    uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+    u += 0x0FFFFFFFFFFFull + ((u >> 45) & 1ull);
+    u &= ~0x1FFFFFFFFFFFull;
+    return static_cast<uint16_t>(__float_as_uint(static_cast<float>(__longlong_as_double((long long)u))) >> 16);
+}
+// rotated values straight from float64: one rounding to the storage type
+__device__ __forceinline__ void store4d(float* p, const double (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+}
+__device__ __forceinline__ void store4d(bf16_t* p, const double (&x)[4]) {
+    uint2 v;
+    v.x = f64_to_bf16(x[0]) | ((uint32_t)f64_to_bf16(x[1]) << 16);
+    v.y = f64_to_bf16(x[2]) | ((uint32_t)f64_to_bf16(x[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+}
+
 constexpr int kReorderThreads = 512;
 
 template <typename T>
@@ -164,15 +192,17 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderAr
                 const int j = isq ? it : it - qn;
                 const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
                 T* dst = isq ? qd + (size_t)hh * D + c : kc + (row0 + (size_t)hh * kPage) * D + c;
-                float y0[4], y1[4];
+                // x cos - y sin and y cos + x sin in float64, each rounded
+                // once to the storage type
+                double y[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double cs = s_cs[c + e], sn = s_sn[c + e];
-                    y0[e] = (float)((double)x0[u][e] * cs - (double)x1[u][e] * sn);
-                    y1[e] = (float)((double)x1[u][e] * cs + (double)x0[u][e] * sn);
-                }
-                store4(dst, y0);
-                store4(dst + half, y1);
+                for (int e = 0; e < 4; ++e)
+                    y[e] = (double)x0[u][e] * s_cs[c + e] - (double)x1[u][e] * s_sn[c + e];
+                store4d(dst, y);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = (double)x1[u][e] * s_cs[c + e] + (double)x0[u][e] * s_sn[c + e];
+                store4d(dst + half, y);
             } else {
                 const int j = it - qn - kn;
                 const int g = j / (D / 4), d = (j % (D / 4)) * 4;

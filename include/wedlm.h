@@ -95,8 +95,8 @@ typedef struct {
  * wedlm_reorder -- Topological Reordering + logical RoPE + KV append.
  * (paper-summary page, "Key claims", sec. 4.1 Eq. 5-6: observed tokens move
  * to the physical front while RoPE keeps their logical positions; "Method",
- * inference paragraph: each step reorders the window so filled tokens come
- * first and runs causally on the persistent cache.)
+ * inference paragraph: the decode window is put in this order before every
+ * causal pass over the cached prefix.)
  *
  * For each sequence b the physical order is: filled slots in slot order,
  * then masked slots in slot order (perm[b][r] = logical slot at physical

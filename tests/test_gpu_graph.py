@@ -1,20 +1,26 @@
 """Decode steps captured in a HIP graph replay exactly like the same steps
 run eagerly -- captured by torch and by the library's own capture API
-(wedlm_graph_*).
+(wedlm_graph_*) -- and both match the oracle.
 
 Three whole steps (reorder, attention, select/commit) on the Qwen3-8B-shaped
 single-layer workload are captured once and replayed four times, each replay
 from the same restored state, with eager work and synchronisation of the
 program between replays.  Every replay must reproduce the eager run's bytes:
 committed counts and tokens, attention outputs, window state and the K/V
-cache.  None of the library's calls allocates, synchronises or clears memory,
-so the whole step can sit in a graph."""
+cache.  The eager run itself is checked against the oracle streamed over
+the same three steps (reorder, attention over the grown cache, select /
+commit / refill): integer state and commits exactly, attention within the
+bf16 tolerance, the appended K bit-exact (up to the rounding-tie band of the
+reorder parity test) and V exactly.  None of the library's calls allocates,
+synchronises or clears memory, so the whole step can sit in a graph."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as wl
 import causal_attention_diffusion_amd as wd
+from parity_checks import rounding_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +64,63 @@ def _decode_setup(dev, steps=3, V=4096):
     def snapshot():
         return [x.clone() for x in (n_commit, committed, outs, counters) + state]
 
-    return t, run, restore, snapshot, n_commit
+    def check_oracle(snap):
+        _check_against_oracle(inp, cfg, scfg, [lg.cpu().numpy() for lg in logits], snap)
+
+    return t, run, restore, snapshot, n_commit, check_oracle
+
+
+def _check_against_oracle(inp, cfg, scfg, logits, snap):
+    """Stream the oracle over the same steps and compare with the eager
+    run's snapshot (n_commit, committed, outs, counters, tok, filled, pos,
+    ctx_len, k_cache, v_cache)."""
+    g_nc, g_cm, g_out, g_cnt, g_tok, g_filled, g_pos, g_ctx, g_kc, g_vc = [x.cpu() for x in snap]
+    dt, B, W, V = cfg.dtype, cfg.B, cfg.W, scfg.V
+    f64 = lambda a: wl.storage_to_f64(a, dt)
+    q, k, v = f64(inp.q), f64(inp.k), f64(inp.v)
+    tok = np.where(inp.filled == 1, 5, V).astype(np.int32)
+    filled, pos, ctx = inp.filled.copy(), inp.pos.copy(), inp.ctx_len.copy()
+    cache_k = [f64(inp.prefix_k[b]) for b in range(B)]
+    cache_v = [f64(inp.prefix_v[b]) for b in range(B)]
+    cache_k64 = [x.copy() for x in cache_k]
+    hist = []
+    for i, lg in enumerate(logits):
+        perm, qp, kw, vw = oracle.reorder(filled, pos, q, k, v, dt, cfg.rope_base)
+        _, _, kw64, _ = oracle.reorder(filled, pos, q, k, v, "f64", cfg.rope_base)
+        dk = [np.concatenate([cache_k[b][:ctx[b]], kw[b]]) for b in range(B)]
+        dv = [np.concatenate([cache_v[b][:ctx[b]], vw[b]]) for b in range(B)]
+        dk64 = [np.concatenate([cache_k64[b][:ctx[b]], kw64[b]]) for b in range(B)]
+        out = oracle.attention(qp, dk, dv, ctx, perm)
+        err = float(np.abs(f64_t(g_out[i], dt) - out).max() / np.abs(out).max())
+        assert err <= 2e-2, (i, err)
+        sel = oracle.select_commit(lg, tok, filled, pos, ctx, scfg.alpha, scfg.tau, V)
+        assert (sel["margin"] > 1e-4).all(), sel["margin"]
+        np.testing.assert_array_equal(g_nc[i].numpy(), sel["n_commit"])
+        np.testing.assert_array_equal(g_cm[i].numpy(), sel["committed"])
+        hist.append(sel["n_commit"])
+        tok, filled, pos, ctx = sel["tok"], sel["filled"], sel["pos"], sel["ctx_len"]
+        cache_k, cache_v, cache_k64 = dk, dv, dk64
+        print(f"[graph oracle] step {i}: attention err {err:.3e}, commits {sel['n_commit'].tolist()}", flush=True)
+    np.testing.assert_array_equal(g_tok.numpy(), tok)
+    np.testing.assert_array_equal(g_filled.numpy(), filled)
+    np.testing.assert_array_equal(g_pos.numpy(), pos)
+    np.testing.assert_array_equal(g_ctx.numpy(), ctx)
+    n_new, n_total, _ = oracle.prefix_cacheability(hist, W)
+    np.testing.assert_array_equal(g_cnt.numpy(), np.stack([n_new, n_total], axis=1))
+    # every cache row the steps wrote: the committed ones and the last window
+    for b in range(B):
+        L0 = int(inp.ctx_len[b])
+        t = np.arange(L0, cache_k[b].shape[0])
+        pages = inp.block_table[b, t // wl.PAGE].astype(np.int64)
+        slot = (t % wl.PAGE).astype(np.int64)
+        gk = f64_t(g_kc[pages, :, slot, :], dt)
+        gv = f64_t(g_vc[pages, :, slot, :], dt)
+        rounding_exact(gk, cache_k[b][L0:], cache_k64[b][L0:])
+        np.testing.assert_array_equal(gv, cache_v[b][L0:])
+
+
+def f64_t(x, dt):
+    return wl.torch_storage_to_f64(x, dt)
 
 
 def _replays_match(replay, restore, snapshot, ref, dev):
@@ -75,11 +137,12 @@ def _replays_match(replay, restore, snapshot, ref, dev):
 
 def test_captured_steps_replay_like_eager(dev):
     print("[graph] qwen3_l2048 x3 steps, V=4096, torch capture", flush=True)
-    t, run, restore, snapshot, n_commit = _decode_setup(dev)
+    t, run, restore, snapshot, n_commit, check_oracle = _decode_setup(dev)
     run()
     torch.cuda.synchronize()
     ref = snapshot()
     assert int(n_commit.sum().item()) > 0          # the steps did commit something
+    check_oracle(ref)
 
     restore()
     graph = torch.cuda.CUDAGraph()
@@ -99,10 +162,11 @@ def test_native_capture_replays_like_eager(dev):
     # three steps = 15 kernel nodes (reorder, split attention, combine,
     # vocabulary statistics, commit) and nothing else -- no memset nodes
     print("[graph] qwen3_l2048 x3 steps, V=4096, native capture", flush=True)
-    t, run, restore, snapshot, n_commit = _decode_setup(dev)
+    t, run, restore, snapshot, n_commit, check_oracle = _decode_setup(dev)
     run()
     torch.cuda.synchronize()
     ref = snapshot()
+    check_oracle(ref)
     restore()
     torch.cuda.synchronize()
     cap = torch.cuda.Stream()

@@ -5,9 +5,13 @@ entry points through the Python binding on the GPU and compares with the
 oracle on the same input bytes:
   * integer outputs (permutation, argmax, commit set, window state) bit-exact;
   * attention outputs: max |gpu - oracle| / max |oracle| <= 1e-4 (fp32) and
-    2e-2 (bf16);
-  * rotated queries/keys within one storage ulp, values copied bit-exactly.
-Large workloads are checked on sampled rows the oracle computes one by one.
+    2e-2 (bf16), over every output row of every workload;
+  * rotated queries/keys bit-exact: both sides round the float64 rotation
+    once to the storage type.  The two compute the angle by different
+    routes (p * 2^(-2c/D log2 base) vs p * base^(-2c/D)), which agree to
+    about 1e-12 relative, so an element whose float64 value lies within
+    1e-9 relative of a rounding tie may take either neighbour; every other
+    element must be identical.  Values are copied bit-exactly.
 """
 import numpy as np
 import pytest
@@ -16,6 +20,7 @@ import torch
 import oracle
 import workloads as wl
 import causal_attention_diffusion_amd as wd
+from parity_checks import rounding_exact
 
 pytestmark = pytest.mark.gpu
 
@@ -25,12 +30,6 @@ ATTN_CFGS = ["tiny_f32", "qwen3_l2048", "ragged_b32", "long_b4"]
 
 def rel_err(got, ref):
     return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
-
-
-def ulp_ok(got, ref, dtype):
-    # one storage ulp: 2^-7 relative for bf16 (8 significant bits), 2^-22 for fp32
-    rel = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -22
-    return np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-30)
 
 
 def run_reorder(t, cfg):
@@ -84,11 +83,12 @@ def test_reorder_parity(name, dev):
     torch.cuda.synchronize()
     assert t["status"].item() == 0
     dt = cfg.dtype
-    perm, qp, kw, vw = oracle.reorder(inp.filled, inp.pos, wl.storage_to_f64(inp.q, dt),
-                                      wl.storage_to_f64(inp.k, dt), wl.storage_to_f64(inp.v, dt),
-                                      dt, cfg.rope_base)
+    args = (inp.filled, inp.pos, wl.storage_to_f64(inp.q, dt), wl.storage_to_f64(inp.k, dt),
+            wl.storage_to_f64(inp.v, dt))
+    perm, qp, kw, vw = oracle.reorder(*args, dt, cfg.rope_base)
+    _, qp64, kw64, _ = oracle.reorder(*args, "f64", cfg.rope_base)   # unrounded rotation
     np.testing.assert_array_equal(t["perm"].cpu().numpy(), perm)
-    assert ulp_ok(wl.torch_storage_to_f64(t["q_phys"], dt), qp, dt)
+    ties = rounding_exact(wl.torch_storage_to_f64(t["q_phys"], dt), qp, qp64)
     touched = torch.zeros(t["k_cache"].shape[:1] + t["k_cache"].shape[2:3], dtype=torch.bool, device=dev)
     for b in range(cfg.B):
         L = int(inp.ctx_len[b])
@@ -98,8 +98,9 @@ def test_reorder_parity(name, dev):
         touched[pages, slots] = True
         gk = t["k_cache"][pages, :, slots, :]          # [W, Hkv, D]
         gv = t["v_cache"][pages, :, slots, :]
-        assert ulp_ok(wl.torch_storage_to_f64(gk, dt), kw[b], dt)
+        ties += rounding_exact(wl.torch_storage_to_f64(gk, dt), kw[b], kw64[b])
         np.testing.assert_array_equal(wl.torch_storage_to_f64(gv, dt), vw[b])
+    print(f"[reorder] {name}: q_phys and appended K bit-exact ({ties} tie-band elements)")
     # nothing outside the window's rows changed (committed K/V never move)
     keep = ~touched
     assert torch.equal(t["k_cache"].permute(0, 2, 1, 3)[keep], kc0.permute(0, 2, 1, 3)[keep])
@@ -147,7 +148,7 @@ def _attn_alone(cfg, dev, n_rows=None, seed=None):
 
 
 @pytest.mark.parametrize("name,n_rows", [("tiny_f32", None), ("qwen3_l2048", None),
-                                         ("ragged_b32", 384), ("long_b4", 192)])
+                                         ("ragged_b32", None), ("long_b4", None)])
 def test_attention_parity(name, n_rows, dev):
     cfg = wl.CONFIGS[name]
     print(f"[attn] {name}", flush=True)
@@ -172,7 +173,7 @@ def test_attention_at_maximum_context(dev):
 
 # ---------------------------------------------------------------- reorder + attention
 @pytest.mark.parametrize("name,n_rows", [("tiny_f32", None), ("qwen3_l2048", None),
-                                         ("ragged_b32", 256), ("long_b4", 128)])
+                                         ("ragged_b32", None), ("long_b4", None)])
 def test_decode_step_parity(name, n_rows, dev):
     cfg = wl.CONFIGS[name]
     print(f"[step] {name}", flush=True)
