@@ -40,6 +40,8 @@ from .binding import (  # noqa: F401
     wedlm_select_commit_workspace,
     wedlm_set_attn_split_keys,
     wedlm_step_attn,
+    wedlm_step_attn_noalloc,
+    wedlm_step_attn_noalloc_limit,
     wedlm_step_attn_workspace,
     wedlm_version,
 )

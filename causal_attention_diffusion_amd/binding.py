@@ -62,6 +62,10 @@ def load_library():
     lib.wedlm_step_attn_workspace.restype = sz
     lib.wedlm_step_attn.argtypes = [S, P, P, P, P, P, P, P, C.c_float, i32, P, sz, P, P]
     lib.wedlm_step_attn.restype = C.c_int
+    lib.wedlm_step_attn_noalloc.argtypes = [S, P, P, P, P, P, P, P, C.c_float, i32, P, P]
+    lib.wedlm_step_attn_noalloc.restype = C.c_int
+    lib.wedlm_step_attn_noalloc_limit.argtypes = []
+    lib.wedlm_step_attn_noalloc_limit.restype = sz
     lib.wedlm_select_commit_workspace.argtypes = [i32, i32, i32]
     lib.wedlm_select_commit_workspace.restype = sz
     lib.wedlm_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
@@ -214,6 +218,28 @@ def wedlm_step_attn(q_phys, k_cache, v_cache, block_table, ctx_len, perm, out, m
         C.byref(s), _ptr(q_phys), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_len),
         _ptr(perm), _ptr(out), float(scale), int(max_ctx_len), _ptr(workspace), ws_bytes,
         _ptr(dev_status), _stream(stream)))
+
+
+def wedlm_step_attn_noalloc(q_phys, k_cache, v_cache, block_table, ctx_len, perm, out, max_ctx_len: int,
+                            scale: float = 0.0, dev_status=None, stream=None):
+    """wedlm_step_attn with the split partials in the library's own device
+    array (no workspace argument; calls on one GPU must not overlap)."""
+    import torch
+    s = _shape_from(q_phys, k_cache, block_table)
+    _expect(k_cache, "k_cache", tuple(k_cache.shape), q_phys.dtype)
+    _expect(v_cache, "v_cache", tuple(k_cache.shape), q_phys.dtype)
+    _expect(block_table, "block_table", tuple(block_table.shape), torch.int32)
+    _expect(ctx_len, "ctx_len", (s.B,), torch.int32)
+    _expect(perm, "perm", (s.B, s.W), torch.int32)
+    _expect(out, "out", tuple(q_phys.shape), q_phys.dtype)
+    _opt(dev_status, "dev_status", (1,), torch.int32)
+    _check(load_library().wedlm_step_attn_noalloc(
+        C.byref(s), _ptr(q_phys), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(ctx_len),
+        _ptr(perm), _ptr(out), float(scale), int(max_ctx_len), _ptr(dev_status), _stream(stream)))
+
+
+def wedlm_step_attn_noalloc_limit() -> int:
+    return int(load_library().wedlm_step_attn_noalloc_limit())
 
 
 def wedlm_attn_plan(q_phys, k_cache, block_table, max_ctx_len: int):

@@ -487,10 +487,74 @@ extern "C" size_t wedlm_step_attn_workspace(const wedlm_shape* s, int32_t max_ct
     return make_plan(s, max_ctx_len).ws_bytes;
 }
 
+static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* ctx_len, const int32_t* perm, void* out, float scale,
+                     int32_t max_ctx_len, void* workspace, size_t ws_bytes, int32_t* dev_status, void* stream);
+
 extern "C" int wedlm_step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* ctx_len, const int32_t* perm, void* out,
                                float scale, int32_t max_ctx_len, void* workspace, size_t ws_bytes,
                                int32_t* dev_status, void* stream) {
+    return step_attn(s, q_phys, k_cache, v_cache, block_table, ctx_len, perm, out, scale, max_ctx_len, workspace,
+                     ws_bytes, dev_status, stream);
+}
+
+// ---------------------------------------------------------------- attention without a caller workspace
+// The split partials of wedlm_step_attn_noalloc live in this file-scope
+// device array (one copy per GPU, kept until the process ends).  In host
+// code `scratch` only names the symbol: its device address on the current
+// GPU comes from hipGetSymbolAddress, taken once per device and cached.
+static constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+static void* scratch_ptr(int* err_dev) {
+    static std::atomic<void*> cache[64];   // per device; threads may race to fill a slot with the same value
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        *err_dev = dev;
+        return nullptr;
+    }
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            *err_dev = dev;
+            return nullptr;
+        }
+        cache[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+extern "C" size_t wedlm_step_attn_noalloc_limit(void) { return kAttnScratchBytes; }
+
+extern "C" int wedlm_step_attn_noalloc(const wedlm_shape* s, const void* q_phys, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_table, const int32_t* ctx_len,
+                                       const int32_t* perm, void* out, float scale, int32_t max_ctx_len,
+                                       int32_t* dev_status, void* stream) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (max_ctx_len < 0) return fail(WEDLM_ERR_ARG, "max_ctx_len must be >= 0");
+    if ((int64_t)max_ctx_len + s->W > kMaxContext)
+        return fail(WEDLM_ERR_UNSUPPORTED, "context of %lld tokens: built for up to %lld",
+                    (long long)max_ctx_len + s->W, (long long)kMaxContext);
+    const size_t need = make_plan(s, max_ctx_len).ws_bytes;
+    if (need > kAttnScratchBytes)
+        return fail(WEDLM_ERR_WORKSPACE,
+                    "wedlm_step_attn_noalloc: this shape needs %zu bytes of split partials, the built-in scratch "
+                    "holds %zu; use wedlm_step_attn with a workspace", need, kAttnScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        int dev = -1;
+        ws = scratch_ptr(&dev);
+        if (!ws) return fail(WEDLM_ERR_HIP, "wedlm_step_attn_noalloc: no scratch address on device %d", dev);
+    }
+    return step_attn(s, q_phys, k_cache, v_cache, block_table, ctx_len, perm, out, scale, max_ctx_len, ws, need,
+                     dev_status, stream);
+}
+
+static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* ctx_len, const int32_t* perm, void* out, float scale,
+                     int32_t max_ctx_len, void* workspace, size_t ws_bytes, int32_t* dev_status, void* stream) {
     int rc = check_shape(s);
     if (rc) return rc;
     if (!q_phys || !k_cache || !v_cache || !block_table || !ctx_len || !perm || !out)

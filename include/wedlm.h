@@ -161,6 +161,29 @@ int wedlm_step_attn(const wedlm_shape *s, const void *q_phys, const void *k_cach
                     void *workspace, size_t ws_bytes, int32_t *dev_status, void *stream);
 
 /*
+ * wedlm_step_attn_noalloc -- wedlm_step_attn without a workspace argument,
+ * for callers that cannot allocate device memory (code recorded into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, result bytes and errors as wedlm_step_attn with the workspace
+ * removed; the split partials go to a library-owned device array of
+ * wedlm_step_attn_noalloc_limit() bytes (32 MiB), one per GPU, held until
+ * the process ends.  The call allocates nothing.
+ *   Errors: as wedlm_step_attn; WEDLM_ERR_WORKSPACE (nothing enqueued) when
+ *   wedlm_step_attn_workspace(s, max_ctx_len) exceeds the limit.
+ *   Concurrency: every call on one GPU shares that GPU's array, so calls
+ *   that may overlap on one GPU (different streams, different host
+ *   threads) race and corrupt each other's results; serialise them (one
+ *   stream) or use wedlm_step_attn with separate workspaces.  Nothing in
+ *   the array needs to start at any value, and a call leaves it holding
+ *   that call's partials.
+ */
+size_t wedlm_step_attn_noalloc_limit(void);
+int wedlm_step_attn_noalloc(const wedlm_shape *s, const void *q_phys, const void *k_cache,
+                            const void *v_cache, const int32_t *block_table, const int32_t *ctx_len,
+                            const int32_t *perm, void *out, float scale, int32_t max_ctx_len,
+                            int32_t *dev_status, void *stream);
+
+/*
  * wedlm_select_commit_workspace -- bytes of device workspace for
  * wedlm_select_commit at (B, W, V): one 16-byte partial per (slot, 16384
  * logits).  Contents need no initialisation and are not preserved; calls
