@@ -24,11 +24,17 @@ from the same starting state, as a serving loop would run them
 of the attention call on the final state, bracketed by HIP events on its
 stream, give the mean launch time the roofline divides the launch's
 algorithmic bytes (K/V of every visible key read once, Q in, O out) by; (3)
-the select/commit call alone, for its own bandwidth.  Before each timed
+the select/commit call alone, for its own bandwidth.  With the default
+workload the line also carries, under "configs", the same measurement of
+the other decode-step workloads (qwen3_l2048: batch 1 over a 2048-token
+prefix; ragged_b32: 32 sequences with prefixes uniform in [512, 8192];
+tiny_f32) and of the select/commit workload select_v152k (batch 64 x
+window 16 over V = 151936), each with its attention roofline fraction
+(--no-extra skips them).  Before each timed
 sequence the same sequence runs untimed from the same starting state for at
-least SETTLE_S seconds (and the attention call ATTN_SETTLE times before its
-leg), because the board reaches steady clocks only after some tenths of a
-second of load.
+least SETTLE_S seconds (and the attention call alone for ATTN_SETTLE_S
+seconds before its leg), because the board reaches steady clocks only
+after some tenths of a second of load.
 """
 import argparse
 import json
@@ -49,7 +55,8 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long_b4.md")
 ATTN_SOURCES = ["attn_bf16.hip", "attn.hip", "api.hip", "kernels.hpp", "common.hpp"]
 METRIC = "window tokens/sec and decode steps/sec per GPU; attn achieved HBM GB/s vs peak"
-ATTN_SETTLE = 100   # untimed attention launches before the roofline leg
+ATTN_SETTLE = 100   # attention launches per untimed round before the roofline leg
+ATTN_SETTLE_S = 0.5 # seconds of such rounds: the call's own steady clocks before it is timed
 SETTLE_S = 0.25     # seconds of untimed repeats of the timed sequence before it is timed
 
 
@@ -70,6 +77,9 @@ def parse():
     ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="long_b4 only: skip the summaries of the other decode-step workloads and of the "
+                         "select/commit workload that the default line carries under \"configs\"")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = auto)")
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: eager, then the same K steps replayed "
@@ -152,12 +162,52 @@ def main():
         bench_model(args)
         return
 
+    result = decode_leg(args, args.workload, with_cpu=not args.no_cpu)
+    if args.workload == "long_b4" and not args.no_extra:
+        # the other workloads of the decode step, each timed the same way
+        # (same --steps / --warmup), summarised beside the headline
+        extra = {}
+        for name in EXTRA_DECODE:
+            extra[name] = summarise_decode(decode_leg(args, name, with_cpu=False))
+            print(f"[bench] {name}: {extra[name]['ms_per_step']} ms per step", file=sys.stderr, flush=True)
+        extra["select_v152k"] = summarise_select(bench_select(args, emit=False))
+        print(f"[bench] select_v152k: {extra['select_v152k']['ms_per_step']} ms per step", file=sys.stderr,
+              flush=True)
+        result["configs"] = extra
+    print(json.dumps(result), flush=True)
+
+
+EXTRA_DECODE = ["qwen3_l2048", "ragged_b32", "tiny_f32"]
+
+
+def summarise_decode(r):
+    """The figures of one decode-step workload kept in the headline line."""
+    a = r["attn"]
+    return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
+            "eager_ms_per_step": r["eager_ms_per_step"], "window_tokens_per_s": r["value"],
+            "steps_per_s": r["steps_per_s"], "split_kv": r["config"]["split_kv"],
+            "attn": {"avg_ms": a["avg_ms"], "alg_bytes_per_launch": a["alg_bytes_per_launch"],
+                     "GB_per_s": a["GB_per_s"], "frac_of_hbm_peak": r["roofline"]["frac"]},
+            "select_commit": r["select_commit"], "P_c": r["P_c"],
+            "dtype": r["dtype"]}
+
+
+def summarise_select(r):
+    return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
+            "eager_ms_per_step": r["eager_ms_per_step"], "window_tokens_per_s": r["value"],
+            "select_commit": r["select_commit"], "frac_of_hbm_peak": r["roofline"]["frac"], "P_c": r["P_c"]}
+
+
+def decode_leg(args, workload, with_cpu):
+    """K streaming decode steps (reorder + attention + select/commit) of one
+    workload, then the attention call and the select/commit call alone;
+    returns the result dict of the bench line."""
     import torch
     import workloads as wl
     import causal_attention_diffusion_amd as wd
 
     dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS[args.workload]
+    cfg = wl.CONFIGS[workload]
     scfg = wl.SelectConfig("bench", B=cfg.B, W=cfg.W, V=args.vocab, seed=1005, alpha=0.25, tau=9.0,
                            steps=0, kind="mixture")
     total_steps = args.steps + args.warmup
@@ -251,13 +301,17 @@ def main():
     # ---- timed region 2: the attention call alone, K launches back to back on
     # the stream it runs on (the state the stream ended in), bracketed by one
     # pair of HIP events on that stream: its mean launch duration for the
-    # roofline.  ATTN_SETTLE untimed launches of the same call come first.
+    # roofline.  Untimed launches of the same call come first, in rounds of
+    # ATTN_SETTLE for ATTN_SETTLE_S seconds.
     # (An event pair around every single call inside the steps would add
     # about 8 us of marker overhead to each measured call.)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for _ in range(ATTN_SETTLE):
-        attention()
+    t_end = time.perf_counter() + ATTN_SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(ATTN_SETTLE):
+            attention()
+        torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
         attention()
@@ -365,16 +419,18 @@ def main():
                      "matches_commit_history": bool(int(cnt[:, 0].sum()) == int(nc.sum())
                                                     and int(cnt[:, 1].sum()) == K * B * W)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(workload),
                      "kernel": "wedlm_step_attn (attn_split + attn_combine)"},
     }
 
-    if not args.no_cpu:
+    if with_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, args, inp)
-    print(json.dumps(result), flush=True)
+    del t, ws_attn, ws_sel, logits
+    torch.cuda.empty_cache()
+    return result
 
 
-def bench_select(args):
+def bench_select(args, emit=True):
     """The select/commit call alone, streaming: batch 64 x window 16 over
     V=151936 fp32 logits, starting from an all-masked window at prefix 0.  A
     step is one wedlm_select_commit (vocabulary statistics of every masked
@@ -467,9 +523,13 @@ def bench_select(args):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "wedlm_select_commit (vocab_stats + commit_select_refill)"},
     }
-    if not args.no_cpu:
+    if emit and not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline_select(cfg, args)
-    print(json.dumps(result), flush=True)
+    del logits, ws
+    torch.cuda.empty_cache()
+    if emit:
+        print(json.dumps(result), flush=True)
+    return result
 
 
 def bench_lmhead(args):
@@ -892,20 +952,20 @@ def attn_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(args):
+def recorded_traffic(workload):
     """Bytes per attention launch from the committed counter summary, or None
-    when the kernel sources or the run differ from the profiled ones."""
+    when the workload or the attention sources differ from the profiled
+    ones (the figure belongs to that kernel build; the context grows by a
+    few hundred tokens over a run, a change of well under 1 %)."""
     try:
         with open(TRAFFIC_FILE) as fh:
             kv = dict(line[2:].split(": ", 1) for line in fh.read().splitlines()
                       if line.startswith("- ") and ": " in line)
     except OSError:
         return None
-    run = {"workload": args.workload, "steps": str(args.steps), "warmup": str(args.warmup),
-           "vocab": str(args.vocab), "split_keys": str(args.split_keys)}
     if kv.get("source_sha256", "").strip("` ") != attn_source_hash():
         return None
-    if any(kv.get(k, "").strip("` ") != v for k, v in run.items()):
+    if kv.get("workload", "").strip("` ") != workload:
         return None
     try:
         return int(kv["traffic_bytes_per_launch"].strip("` "))

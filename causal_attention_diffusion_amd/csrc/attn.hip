@@ -1,5 +1,6 @@
-// attn.hip -- windowed causal grouped-query attention of one WeDLM decode
-// step over a paged prefix KV cache (gfx950, MFMA).
+// attn.hip -- fp32 windowed causal grouped-query attention of one WeDLM
+// decode step over a paged prefix KV cache (gfx950, MFMA), and the split-KV
+// combine shared by the fp32 and bf16 kernels.
 //
 // Pages: "WeDLM: Reconciling Diffusion Language Models with Standard Causal
 // Attention for Fast Inference", paper-summary page, "Key claims" (paper
@@ -16,66 +17,49 @@
 // (b, g, row tile, split); partial (O, m, l) of several splits are merged by
 // attn_combine with the usual log-sum-exp rule.
 //
-// Per work-group the keys stream through LDS in chunks of CHUNK keys with
-// a register-staged double buffer: 16-byte coalesced global loads of whole
-// 4 KB (page, head) blocks, paged through a block-table slice held in LDS.
+// Per work-group the keys stream through LDS in chunks of 32 keys with a
+// register-staged double buffer: 16-byte coalesced global loads of whole
+// (page, head) blocks, paged through a block-table slice held in LDS.
 //
 // Tiles are transposed so that one lane owns one query row:
-//   S^T[key][row] = K[key][:] . Q[row][:]       (A = K from LDS, B = Q in VGPRs)
-//   O^T[d][row]  += V^T[d][key] P^T[key][row]   (A = V^T via ds_read_tr16_b64,
-//                                                B = P straight from S^T's VGPRs)
-// With v_mfma_f32_32x32x16_bf16 a lane's 16 outputs are 16 keys (or 16 d)
-// of one row (lane % 32), so the online-softmax max/sum are in-lane plus
-// one exchange with lane ^ 32, and the O rescale is in-lane.  The key order
-// inside the PV contraction is permuted to match S^T's register layout; the
-// same permutation is applied to V, so the sum is unchanged.
+//   S^T[key][row] = K[key][:] . Q[row][:]       (v_mfma_f32_32x32x2f32:
+//                                                 A = K from LDS, B = Q in VGPRs)
+//   O^T[d][row]  += V^T[d][key] P^T[key][row]   (A = V from LDS, B = P from
+//                                                 S^T's VGPRs)
+// A lane's 16 outputs are 16 keys (or 16 d) of one row (lane % 32), so the
+// online-softmax max/sum are in-lane plus one exchange with lane ^ 32, and
+// the O rescale is in-lane.
 //
-// This file holds the fp32 kernel (v_mfma_f32_32x32x2f32, register-staged
-// double buffer) and the split combine shared by both dtypes; bf16 uses the
-// direct-to-LDS kernel of attn_bf16.hip with the same tile transposition.
-#include <type_traits>
-
+// The bf16 kernels (attn_bf16.hip) use the same transposed tiling with
+// direct global-to-LDS loads.
 #include "kernels.hpp"
 
 namespace wedlm {
 
-
-template <typename T, int D, int NW, int CHUNK>
+template <int D, int NW>
 struct AttnCfg {
+    static constexpr int CHUNK = 32;           // keys per LDS chunk
     static constexpr int NT = 64 * NW;
     static constexpr int RT = 32 * NW;
-    static constexpr int TB = sizeof(T);
-    static constexpr bool BF = TB == 2;
-    static constexpr int KPAD = BF ? 8 : 4;    // elements; K rows 16 B apart in bank space
-    static constexpr int VPAD = BF ? 32 : 4;   // V rows shifted by 16 banks for the transpose reads
-    static constexpr int KS = D + KPAD;
-    static constexpr int VS = D + VPAD;
-    static constexpr int ROWP = D * TB / 16;   // 16-byte pieces per key row
+    static constexpr int KS = D + 4;           // padded K row (floats): rows 16 B apart in bank space
+    static constexpr int VS = D + 4;
+    static constexpr int ROWP = D * 4 / 16;    // 16-byte pieces per key row
     static constexpr int PIECES = CHUNK * ROWP;
     static constexpr int PPT = PIECES / NT;    // pieces per thread per K (or V) chunk
-    static constexpr int NTILE = CHUNK / 32;
     static constexpr int NDT = D / 32;
-    static constexpr int EPP = 16 / TB;        // elements per piece
     static_assert(PIECES % NT == 0, "chunk must split evenly over the threads");
 };
 
-__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ s16x4 lds_read_tr(const void* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
-}
-
-template <typename T, int D, int NW, int CHUNK>
-__global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
-    using C = AttnCfg<T, D, NW, CHUNK>;
-    __shared__ __attribute__((aligned(16))) T s_k[2][CHUNK * C::KS];
-    __shared__ __attribute__((aligned(16))) T s_v[2][CHUNK * C::VS];
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_split_f32(AttnArgs a) {
+    using C = AttnCfg<D, NW>;
+    constexpr int CHUNK = C::CHUNK;
+    __shared__ __attribute__((aligned(16))) float s_k[2][CHUNK * C::KS];
+    __shared__ __attribute__((aligned(16))) float s_v[2][CHUNK * C::VS];
     __shared__ int s_pages[kMaxSplitPages];
 
     const int tid = threadIdx.x;
@@ -129,17 +113,9 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
     const size_t q_off = (((size_t)b * a.W + (row_ok ? r : 0)) * a.Hq + h) * D;
 
     // Q fragments (B operand of S^T = K Q^T), kept in VGPRs
-    constexpr int NQ = C::BF ? D / 16 : D / 2;
-    typedef typename std::conditional<C::BF, bf16x8, float>::type QF;
-    QF qf[NQ];
-    if constexpr (C::BF) {
-        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + q_off);
-#pragma unroll
-        for (int s = 0; s < NQ; ++s) {
-            uint4 v = row_ok ? qp[s * 2 + hl] : make_uint4(0, 0, 0, 0);
-            qf[s] = __builtin_bit_cast(bf16x8, v);
-        }
-    } else {
+    constexpr int NQ = D / 2;
+    float qf[NQ];
+    {
         const float* qp = static_cast<const float*>(a.q) + q_off + hl * (D / 2);
 #pragma unroll
         for (int s = 0; s < NQ; ++s) qf[s] = row_ok ? qp[s] : 0.f;
@@ -169,7 +145,7 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
             int pg = -1;
             if (t < k_end) pg = s_pages[t / kPage - p0];
             if (pg >= 0) {
-                const size_t off = ((((size_t)pg * a.Hkv + kvh) * kPage + (t % kPage)) * D) * C::TB + pc * 16;
+                const size_t off = ((((size_t)pg * a.Hkv + kvh) * kPage + (t % kPage)) * D) * 4 + pc * 16;
                 kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
                 vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
             } else {
@@ -184,8 +160,8 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
             const int piece = tid + i * C::NT;
             const int kc = piece / C::ROWP;
             const int pc = piece - kc * C::ROWP;
-            *reinterpret_cast<uint4*>(&s_k[buf][kc * C::KS + pc * C::EPP]) = kr[i];
-            *reinterpret_cast<uint4*>(&s_v[buf][kc * C::VS + pc * C::EPP]) = vr[i];
+            *reinterpret_cast<uint4*>(&s_k[buf][kc * C::KS + pc * 4]) = kr[i];
+            *reinterpret_cast<uint4*>(&s_v[buf][kc * C::VS + pc * 4]) = vr[i];
         }
     };
 
@@ -199,26 +175,17 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
     for (int c = 0; c < n_chunks; ++c) {
         const int buf = c & 1;
         if (c + 1 < n_chunks) load_chunk(c + 1);
-        const T* sk = s_k[buf];
-        const T* sv = s_v[buf];
+        const float* skb = s_k[buf];
+        const float* svb = s_v[buf];
 
-        // ---- S^T = K Q^T for the chunk's 32-key tiles
-        f32x16 sacc[C::NTILE];
+        // ---- S^T = K Q^T for the chunk's 32 keys
+        f32x16 sacc;
 #pragma unroll
-        for (int tt = 0; tt < C::NTILE; ++tt) {
+        for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+        {
+            const float* krow = skb + col * C::KS;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sacc[tt][e] = 0.f;
-            const T* krow = sk + (tt * 32 + col) * C::KS;
-            if constexpr (C::BF) {
-#pragma unroll
-                for (int s = 0; s < NQ; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + s * 16 + hl * 8);
-                    sacc[tt] = mfma_bf16(kf, qf[s], sacc[tt]);
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < NQ; ++s) sacc[tt] = mfma_f32(krow[s + hl * (D / 2)], qf[s], sacc[tt]);
-            }
+            for (int s = 0; s < NQ; ++s) sacc = mfma_f32(krow[s + hl * (D / 2)], qf[s], sacc);
         }
 
         // ---- online softmax (log2 domain); key of element e: 4*hl + 8*(e/4) + e%4
@@ -226,30 +193,26 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
         const bool need_mask = kb + CHUNK - 1 > L;
         float mx = -INFINITY;
 #pragma unroll
-        for (int tt = 0; tt < C::NTILE; ++tt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float x = sacc[tt][e] * a.scale_log2;
-                if (need_mask) {
-                    const int t = kb + tt * 32 + hl * 4 + (e >> 2) * 8 + (e & 3);
-                    if (t > lim) x = -INFINITY;
-                }
-                sacc[tt][e] = x;
-                mx = fmaxf(mx, x);
+        for (int e = 0; e < 16; ++e) {
+            float x = sacc[e] * a.scale_log2;
+            if (need_mask) {
+                const int t = kb + hl * 4 + (e >> 2) * 8 + (e & 3);
+                if (t > lim) x = -INFINITY;
             }
+            sacc[e] = x;
+            mx = fmaxf(mx, x);
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_use);
         float lsum = 0.f;
 #pragma unroll
-        for (int tt = 0; tt < C::NTILE; ++tt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = exp2f(sacc[tt][e] - m_use);
-                sacc[tt][e] = p;
-                lsum += p;
-            }
+        for (int e = 0; e < 16; ++e) {
+            const float p = exp2f(sacc[e] - m_use);
+            sacc[e] = p;
+            lsum += p;
+        }
         l_run = l_run * alpha + lsum;
         m_run = m_new;
         if (__any(alpha != 1.f)) {
@@ -261,36 +224,11 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
 
         // ---- O^T += V^T P^T
 #pragma unroll
-        for (int tt = 0; tt < C::NTILE; ++tt) {
-            if constexpr (C::BF) {
+        for (int e = 0; e < 16; ++e) {
+            const int key = hl * 4 + (e >> 2) * 8 + (e & 3);
+            const float* vrow = svb + key * C::VS;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    bf16x8 pf;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sacc[tt][kk * 8 + e];
-                    // transpose-read source row/col of this lane (16-lane groups)
-                    const int key0 = tt * 32 + kk * 16 + hl * 4 + ((lane & 15) >> 2);
-                    const int dsub = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-#pragma unroll
-                    for (int dt = 0; dt < C::NDT; ++dt) {
-                        const T* p_lo = sv + key0 * C::VS + dt * 32 + dsub;
-                        const T* p_hi = p_lo + 8 * C::VS;
-                        const s16x4 lo = lds_read_tr(p_lo);
-                        const s16x4 hi = lds_read_tr(p_hi);
-                        const bf16x8 vf = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        oacc[dt] = mfma_bf16(vf, pf, oacc[dt]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = tt * 32 + hl * 4 + (e >> 2) * 8 + (e & 3);
-                    const float* vrow = reinterpret_cast<const float*>(sv) + key * C::VS;
-#pragma unroll
-                    for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = mfma_f32(vrow[dt * 32 + col], sacc[tt][e], oacc[dt]);
-                }
-            }
+            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = mfma_f32(vrow[dt * 32 + col], sacc[e], oacc[dt]);
         }
 
         if (c + 1 < n_chunks) store_chunk(buf ^ 1);
@@ -308,22 +246,14 @@ __global__ __launch_bounds__(64 * NW) void attn_split(AttnArgs a) {
             return;
         }
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        T* o = static_cast<T*>(a.out) + (((size_t)b * a.W + slot) * a.Hq + h) * D;
+        float* o = static_cast<float*>(a.out) + (((size_t)b * a.W + slot) * a.Hq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d = dt * 32 + hl * 4 + g4 * 8;
-                if constexpr (C::BF) {
-                    uint2 pk;
-                    pk.x = f32_to_bf16(oacc[dt][g4 * 4 + 0] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][g4 * 4 + 1] * inv) << 16);
-                    pk.y = f32_to_bf16(oacc[dt][g4 * 4 + 2] * inv) | ((uint32_t)f32_to_bf16(oacc[dt][g4 * 4 + 3] * inv) << 16);
-                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(o) + d) = pk;
-                } else {
-                    float4 v4 = make_float4(oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv,
-                                            oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv);
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(o) + d) = v4;
-                }
+                *reinterpret_cast<float4*>(o + d) = make_float4(oacc[dt][g4 * 4 + 0] * inv, oacc[dt][g4 * 4 + 1] * inv,
+                                                                oacc[dt][g4 * 4 + 2] * inv, oacc[dt][g4 * 4 + 3] * inv);
             }
     } else {
         const size_t prow = ((size_t)pid * a.nsplit + split) * C::RT + m_loc;
@@ -436,7 +366,7 @@ static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
 template <int D, int NW>
 static hipError_t launch_f32_t(const AttnArgs& a, hipStream_t st) {
     const int npid = a.B * a.Hkv * a.row_tiles;
-    hipLaunchKernelGGL((attn_split<float, D, NW, 32>), dim3((unsigned)npid * a.nsplit), dim3(64 * NW), 0, st, a);
+    hipLaunchKernelGGL((attn_split_f32<D, NW>), dim3((unsigned)npid * a.nsplit), dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
 

@@ -237,12 +237,10 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + q_off);
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
+            // the stored bf16 query as it is: q . k is accumulated exactly
+            // in fp32 and scaled (softmax scale * log2 e) in fp32 at the exp
             const uint4 v = row_ok ? qp[s * 2 + hl] : make_uint4(0, 0, 0, 0);
-            // Q scaled by softmax scale * log2(e) and rounded to bf16 once, so
-            // S comes out of the MFMA in log2 units
-            const bf16x8 raw = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)raw[e] * a.scale_log2);
+            qf[s] = __builtin_bit_cast(bf16x8, v);
         }
     }
     f32x16 oacc[C::NDT];
@@ -251,14 +249,10 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
     // Softmax state of this lane's row: the reference m_ref (log2 units),
-    // applied through the QK accumulator's initial value -m_ref (negm, one
-    // copy per accumulator element), whether the row has seen a visible key
-    // yet, and the running sum l_run.
+    // whether the row has seen a visible key yet, and the running sum l_run.
+    const float sl2 = a.scale_log2;
     float m_ref = 0.f, l_run = 0.f;
     bool started = false;
-    f32x16 negm;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) negm[e] = 0.f;
 
     __syncthreads();  // s_pages visible; Q loads may still be in flight (waited below)
     wait_vm<0>();     // the Q loads count in vmcnt: retire them before the ring accounting starts
@@ -374,7 +368,10 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         bf16x8 kf[D / 16];
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + swz_k(key, 2 * s + hl, C::RC) * 16);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], negm, 0, 0, 0);   // starts at -m_ref
+        f32x16 zero;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], zero, 0, 0, 0);
 #pragma unroll
         for (int s = 1; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
         const int tb = k_begin + st * C::SK + tt_w * 32;   // first key of the tile
@@ -388,8 +385,9 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     };
 
     // Online softmax in the log2 domain with a lazily moved reference.  The
-    // accumulator already holds S - m_ref, so P = 2^(S - m_ref) is one
-    // v_exp per score (sm_core, branch-free: it is interleaved with MFMAs).
+    // accumulator holds q . k, so P = 2^(q . k * scale log2 e - m_ref) is one
+    // FMA and one v_exp per score (sm_core, branch-free: it is interleaved
+    // with MFMAs).
     // The reference only has to keep P in range: sm_finish moves it when a
     // row has not seen a visible key yet or when this lane's 16 P sum past
     // 2^kLazy (so every P <= 2^kLazy holds, as with a max test; inf and NaN
@@ -413,7 +411,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kk * 8 + e]);
+            for (int e = 0; e < 8; ++e) pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kk * 8 + e], sl2, -m_ref));
         lsum = p_sum(pn);
         need = !started || !(lsum <= kLazyP);
     };
@@ -422,7 +420,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
             float mx = sacc[0];
 #pragma unroll
             for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-            mx = fmaxf(mx, other_half(mx, hl)) + m_ref;              // true tile maximum
+            mx = fmaxf(mx, other_half(mx, hl)) * sl2;                // true tile maximum (log2 units)
             const bool vis = mx != -INFINITY;
             const float m_new = started ? (mx > m_ref + kLazy ? mx : m_ref) : (vis ? mx : m_ref);
             if (__any(m_new != m_ref)) {
@@ -434,16 +432,14 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
             }
-            const float sh = m_ref - m_new;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(sacc[kk * 8 + e] + sh);
+                for (int e = 0; e < 8; ++e)
+                    pn[kk][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kk * 8 + e], sl2, -m_new));
             lsum = p_sum(pn);
             m_ref = m_new;
             started = started || vis;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) negm[e] = -m_ref;
         }
         l_run += lsum;
     };

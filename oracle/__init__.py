@@ -130,7 +130,9 @@ def attention(q_phys, dense_k: Sequence[np.ndarray], dense_v: Sequence[np.ndarra
     if rows is None:
         n, rp = 0, None
     else:
-        rows = _c(rows, np.int32).reshape(-1, 3)
+        # each listed output row is computed once (a row listed twice would
+        # have two threads accumulating into the same output)
+        rows = _c(np.unique(np.asarray(rows, np.int32).reshape(-1, 3), axis=0), np.int32)
         n, rp = rows.shape[0], rows
     _lib().wo_attention(B, W, Hq, Hkv, D, float(scale), _p(q_phys), _p(K), _p(V), _p(off),
                         _p(ctx_len), _p(perm), n, _p(rp), _p(out))

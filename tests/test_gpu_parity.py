@@ -125,8 +125,12 @@ def test_reorder_retry_is_idempotent(dev):
 
 
 # ---------------------------------------------------------------- attention alone
-def _attn_alone(cfg, dev, n_rows=None, seed=None):
+def _attn_alone(cfg, dev, n_rows=None, seed=None, loud_keys=()):
     inp, q_phys, dk, dv = wl.make_full_cache_inputs(cfg, seed)
+    for t, f in loud_keys:          # (token, factor): that key of every sequence scaled
+        for b in range(cfg.B):
+            if t < dk[b].shape[0]:
+                dk[b][t] = wl.to_storage(wl.storage_to_f64(dk[b][t], cfg.dtype) * f, cfg.dtype)
     perm = oracle.reorder_perm(inp.filled)
     kc, vc = wl.paged_cache(inp, dk, dv)
     dt = cfg.dtype
@@ -154,6 +158,31 @@ def test_attention_parity(name, n_rows, dev):
     print(f"[attn] {name}", flush=True)
     err, status = _attn_alone(cfg, dev, n_rows)
     print(f"[attn] {name}: max|gpu-oracle|/max|oracle| = {err:.3e} (tol {ATTN_TOL[cfg.dtype]})")
+    assert status == 0
+    assert err <= ATTN_TOL[cfg.dtype], err
+
+
+LOUD = [
+    # (label, config overrides, keys scaled by a factor): a few keys with
+    # scores of tens of nats -- attention-sink-like logits -- in the first
+    # tile, in the middle of a split, late in the prefix and in the window;
+    # the softmax reference must move mid-stream, and the scores must not be
+    # rounded to bf16 before the exponential
+    ("M128_x20", dict(B=2, W=32, L=4096, n_obs=16), ((5, 20.0), (1500, 20.0), (3000, 20.0), (4100, 20.0))),
+    ("M128_x60", dict(B=2, W=32, L=4096, n_obs=16), ((3000, 60.0), (3500, 120.0))),
+    ("M128_late_x60", dict(B=2, W=32, L=4096, n_obs=16), ((4100, 60.0),)),
+    ("M64_x20", dict(B=3, W=16, L=3000, n_obs=4), ((0, 20.0), (777, 20.0), (2999, 20.0), (3005, 20.0))),
+    ("f32_M32_x20", dict(B=2, W=8, L=2000, n_obs=3, Hq=8, Hkv=2, D=64, dtype="f32",
+                         positions=("contiguous",), rope_base=1e4), ((3, 20.0), (1000, 30.0), (2003, 20.0))),
+]
+
+
+@pytest.mark.parametrize("label,over,loud", LOUD, ids=[x[0] for x in LOUD])
+def test_attention_large_scores(label, over, loud, dev):
+    cfg = _cfg("qwen3_l2048", name=label, **over)
+    print(f"[loud] {label}", flush=True)
+    err, status = _attn_alone(cfg, dev, loud_keys=loud)
+    print(f"[loud] {label}: max|gpu-oracle|/max|oracle| = {err:.3e} (tol {ATTN_TOL[cfg.dtype]})")
     assert status == 0
     assert err <= ATTN_TOL[cfg.dtype], err
 
