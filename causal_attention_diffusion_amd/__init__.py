@@ -39,6 +39,7 @@ from .binding import (  # noqa: F401
     wedlm_select_commit,
     wedlm_select_commit_workspace,
     wedlm_set_attn_split_keys,
+    wedlm_set_select_parts,
     wedlm_step_attn,
     wedlm_step_attn_noalloc,
     wedlm_step_attn_noalloc_limit,

@@ -90,6 +90,8 @@ def load_library():
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
     lib.wedlm_set_attn_split_keys.restype = C.c_int
+    lib.wedlm_set_select_parts.argtypes = [i32]
+    lib.wedlm_set_select_parts.restype = C.c_int
     lib.wedlm_graph_begin.argtypes = [P]
     lib.wedlm_graph_begin.restype = C.c_int
     lib.wedlm_graph_end.argtypes = [P, C.POINTER(C.c_void_p)]
@@ -258,6 +260,10 @@ def attn_plan(B, W, Hq, Hkv, D, max_pages, num_pages, dtype, max_ctx_len):
 
 def wedlm_set_attn_split_keys(keys: int):
     _check(load_library().wedlm_set_attn_split_keys(int(keys)))
+
+
+def wedlm_set_select_parts(parts: int):
+    _check(load_library().wedlm_set_select_parts(int(parts)))
 
 
 def wedlm_select_commit_workspace(B: int, W: int, V: int) -> int:

@@ -585,21 +585,38 @@ static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cac
 }
 
 // ---------------------------------------------------------------- select / commit
-static const int kPartLen = 16384;  // most logits per work-group: 256 threads x 16 float4
+static const int kPartLen = 16384;   // most logits per work-group: 256 threads x 16 float4
+static std::atomic<int32_t> g_parts_override{0};   // process-wide, read by every select plan
 
-// Parts of a row: as few as kPartLen allows, of equal length (a multiple of
-// 4) so that no work-group is left with a short tail.
-static void select_plan(int32_t V, int* nparts, int* part_len) {
-    const int np = (V + kPartLen - 1) / kPartLen;
+// Parts of a row: as few as kPartLen allows.  A vocab_stats work-group's
+// time is mostly latency (the slot flag, then one round of 16 loads per
+// thread), so more, shorter parts only add work-groups: on a 151936-logit
+// vocabulary 10 parts beat 16 to 64 at every window size measured (1 x 16
+// up to 64 x 16 slots).  Equal lengths (multiples of 4) so that no
+// work-group is left with a short tail.
+static void select_plan(int32_t B, int32_t W, int32_t V, int* nparts, int* part_len) {
+    (void)B; (void)W;
+    int np = (V + kPartLen - 1) / kPartLen;
+    const int32_t forced = g_parts_override.load(std::memory_order_relaxed);
+    if (forced > np) np = forced;
+    if (np > (V + 3) / 4) np = (V + 3) / 4;                 // at least 4 logits per part
+    if (np < 1) np = 1;
     const int pl = ((V + np - 1) / np + 3) / 4 * 4;
     *part_len = pl;
     *nparts = (V + pl - 1) / pl;
 }
 
+extern "C" int wedlm_set_select_parts(int32_t parts) {
+    if (parts < 0 || parts > 4096) return fail(WEDLM_ERR_ARG, "select parts must be 0 or in [1, 4096], got %d", parts);
+    g_parts_override.store(parts, std::memory_order_relaxed);
+    g_err[0] = 0;
+    return WEDLM_OK;
+}
+
 extern "C" size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V) {
     if (B < 1 || W < 1 || W > 64 || V < 1) return 0;
     int np, pl;
-    select_plan(V, &np, &pl);
+    select_plan(B, W, V, &np, &pl);
     return ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256;
 }
 
@@ -610,15 +627,17 @@ extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float*
                                    void* stream) {
     if (B < 1 || W < 1 || W > 64 || V < 1)
         return fail(WEDLM_ERR_SHAPE, "need B >= 1, 1 <= W <= 64, V >= 1 (B=%d W=%d V=%d)", B, W, V);
-    if ((int64_t)B * W * ((V + kPartLen - 1) / kPartLen) > (1ll << 30)) return fail(WEDLM_ERR_SHAPE, "grid too large");
+    int np, pl;
+    select_plan(B, W, V, &np, &pl);
+    // the dispatch counts work-items in 32 bits: at most 2^24 - 1 work-groups of 256
+    if ((int64_t)B * W * np > (1ll << 24) - 1 || V > (1 << 30))
+        return fail(WEDLM_ERR_SHAPE, "grid too large (B=%d W=%d parts=%d)", B, W, np);
     if (!logits || !tok || !filled || !pos || !ctx_len || !n_commit || !committed)
         return fail(WEDLM_ERR_ARG, "wedlm_select_commit: NULL device pointer");
     if (!isfinite(alpha) || !isfinite(tau)) return fail(WEDLM_ERR_ARG, "alpha and tau must be finite");
     const size_t need = wedlm_select_commit_workspace(B, W, V);
     if (!workspace || ws_bytes < need)
         return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : 0);
-    int np, pl;
-    select_plan(V, &np, &pl);
     SelectArgs a;
     a.logits = logits; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
     a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;

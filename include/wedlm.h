@@ -185,11 +185,23 @@ int wedlm_step_attn_noalloc(const wedlm_shape *s, const void *q_phys, const void
 
 /*
  * wedlm_select_commit_workspace -- bytes of device workspace for
- * wedlm_select_commit at (B, W, V): one 16-byte partial per (slot, 16384
- * logits).  Contents need no initialisation and are not preserved; calls
- * that run at the same time must not share one workspace.
+ * wedlm_select_commit at (B, W, V): one 16-byte partial per slot and
+ * vocabulary part (a row is cut into ceil(V / 16384) parts of equal
+ * length unless wedlm_set_select_parts asks for more).  Contents need no
+ * initialisation and are not preserved; calls that run at the same time
+ * must not share one workspace.
  */
 size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V);
+
+/*
+ * wedlm_set_select_parts -- process-wide override of the vocabulary parts
+ * per row (1..4096; still at least V / 16384 and at most V / 4), 0 restores
+ * the automatic choice.  Affects later workspace queries and calls alike,
+ * so a workspace sized before a change may be too small after it (the call
+ * then fails with WEDLM_ERR_WORKSPACE).  A tuning knob; results agree with
+ * the automatic plan up to the rounding order of the merged sums.
+ */
+int wedlm_set_select_parts(int32_t parts);
 
 /*
  * wedlm_select_commit -- confidence, commit, Eq. 11 select and refill.
@@ -224,7 +236,8 @@ size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V);
  *   counters [B][2] int64 device, accumulated in place (the caller zeroes
  *            it at the start of a stream), or NULL
  *   workspace / ws_bytes  see wedlm_select_commit_workspace
- * Logits must be finite.  W <= 64, V >= 1.
+ * Logits must be finite.  W <= 64, V >= 1, and B * W * parts below 2^24
+ * (WEDLM_ERR_SHAPE otherwise).
  */
 int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float *logits, int32_t *tok,
                         uint8_t *filled, int32_t *pos, int32_t *ctx_len, int32_t *n_commit,

@@ -463,6 +463,28 @@ def test_select_stream_small_free_running(B, W, V, dev):
     np.testing.assert_array_equal(counters.cpu().numpy(), np.stack([n_new, n_total], axis=1))
 
 
+@pytest.mark.parametrize("parts", [3, 37, 200])
+def test_select_forced_parts(parts, dev):
+    """More vocabulary parts than the automatic plan (the commit kernel then
+    merges more than one round of 16 partials per slot): same results."""
+    B, W, V = 2, 24, 40000
+    cfg = wl.SelectConfig("p", B=B, W=W, V=V, seed=99 + parts, alpha=0.25, tau=6.0, steps=4, kind="mixture")
+    tok, filled, pos, ctx = wl.initial_window(B, W, V)
+    wd.wedlm_set_select_parts(parts)
+    try:
+        ws = wd.select_workspace_tensor(B, W, V, dev)
+        st = _state_to_dev(tok, filled, pos, ctx, dev)
+        for step in range(cfg.steps):
+            lg = wl.make_logits_np(cfg, step)
+            ref = oracle.select_commit(lg, tok, filled, pos, ctx, cfg.alpha, cfg.tau, V)
+            outs = _gpu_select(torch.from_numpy(lg).to(dev), st, cfg.alpha, cfg.tau, V, ws)
+            torch.cuda.synchronize()
+            _check_step(ref, st, outs)
+            tok, filled, pos, ctx = ref["tok"], ref["filled"], ref["pos"], ref["ctx_len"]
+    finally:
+        wd.wedlm_set_select_parts(0)
+
+
 def test_select_window_full_commits_all(dev):
     B, W, V = 2, 64, 100
     ws = wd.select_workspace_tensor(B, W, V, dev)
