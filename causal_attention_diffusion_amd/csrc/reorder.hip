@@ -59,15 +59,33 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     u &= ~0x1FFFFFFFFFFFull;
     return static_cast<uint16_t>(__float_as_uint(static_cast<float>(__longlong_as_double((long long)u))) >> 16);
 }
-// rotated values straight from float64: one rounding to the storage type
-__device__ __forceinline__ void store4d(float* p, const double (&x)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+// Rotate 4 pairs (x0[e], x1[e]) by the angles of cos/sin cs[e], sn[e]:
+// x0 cos - x1 sin goes to p[e], x1 cos + x0 sin to p[half + e], each
+// computed in float64 and rounded once to the storage type.  One element at
+// a time, so that few float64 values are live (the bf16 form packs its
+// results as it goes): the kernel stays within 64 VGPRs.
+__device__ __forceinline__ void rotate_store(float* p, int half, const float (&x0)[4], const float (&x1)[4],
+                                             const double* cs, const double* sn) {
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = (float)((double)x0[e] * cs[e] - (double)x1[e] * sn[e]);
+        hi[e] = (float)((double)x1[e] * cs[e] + (double)x0[e] * sn[e]);
+    }
+    *reinterpret_cast<float4*>(p) = make_float4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<float4*>(p + half) = make_float4(hi[0], hi[1], hi[2], hi[3]);
 }
-__device__ __forceinline__ void store4d(bf16_t* p, const double (&x)[4]) {
-    uint2 v;
-    v.x = f64_to_bf16(x[0]) | ((uint32_t)f64_to_bf16(x[1]) << 16);
-    v.y = f64_to_bf16(x[2]) | ((uint32_t)f64_to_bf16(x[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = v;
+__device__ __forceinline__ void rotate_store(bf16_t* p, int half, const float (&x0)[4], const float (&x1)[4],
+                                             const double* cs, const double* sn) {
+    uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t sh = 16u * (e & 1);
+        lo[e >> 1] |= (uint32_t)f64_to_bf16((double)x0[e] * cs[e] - (double)x1[e] * sn[e]) << sh;
+        hi[e >> 1] |= (uint32_t)f64_to_bf16((double)x1[e] * cs[e] + (double)x0[e] * sn[e]) << sh;
+    }
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo[0], lo[1]);
+    *reinterpret_cast<uint2*>(p + half) = make_uint2(hi[0], hi[1]);
 }
 
 constexpr int kReorderThreads = 512;
@@ -192,17 +210,7 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderAr
                 const int j = isq ? it : it - qn;
                 const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
                 T* dst = isq ? qd + (size_t)hh * D + c : kc + (row0 + (size_t)hh * kPage) * D + c;
-                // x cos - y sin and y cos + x sin in float64, each rounded
-                // once to the storage type
-                double y[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = (double)x0[u][e] * s_cs[c + e] - (double)x1[u][e] * s_sn[c + e];
-                store4d(dst, y);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = (double)x1[u][e] * s_cs[c + e] + (double)x0[u][e] * s_sn[c + e];
-                store4d(dst + half, y);
+                rotate_store(dst, half, x0[u], x1[u], s_cs + c, s_sn + c);
             } else {
                 const int j = it - qn - kn;
                 const int g = j / (D / 4), d = (j % (D / 4)) * 4;
