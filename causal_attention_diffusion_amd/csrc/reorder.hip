@@ -7,40 +7,21 @@
 // their logical positions) and "Method" (inference paragraph: the window is
 // reordered with filled tokens first before the causal pass on the cache).
 //
-// One work-group per (logical slot i, sequence b).  It loads the rows of
-// slot i at once, and meanwhile each wave derives the slot's physical row
-// with two ballots (filled / masked masks) and a prefix popcount: slot i
-// lands at r = popc(filled below i) if filled, else n_obs + popc(masked
-// below i).  The work-group then rotates the Hq query heads and Hkv key
-// heads at the slot's logical position into physical row r and writes the
-// key/value rows into the paged cache at token ctx_len[b] + r.
+// One work-group per (run of SPW logical slots, sequence b): one slot for a
+// decode window, four for the thousands of one-block windows of a
+// Dual-Stream pass.  It loads the rows of its slots at once, and meanwhile
+// each wave derives the slots' physical rows with two ballots (filled /
+// masked masks) and prefix popcounts: slot i lands at r = popc(filled below
+// i) if filled, else n_obs + popc(masked below i).  The work-group then
+// rotates the Hq query heads and Hkv key heads at each slot's logical
+// position into physical row r and writes the key/value rows into the paged
+// cache at token ctx_len[b] + r.
 // The work is tiny (B*W*(Hq+2Hkv)*D elements) and latency-bound; angles and
 // rotations are float64 so that positions up to 2^31 keep full accuracy.
 #include "kernels.hpp"
 
 namespace wedlm {
 
-
-// 4 consecutive elements (8-byte bf16 / 16-byte fp32 access; the offsets
-// used here are multiples of 4 elements, so the accesses are aligned)
-__device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-__device__ __forceinline__ void load4(const bf16_t* p, float (&x)[4]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
-    x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
-}
-__device__ __forceinline__ void store4(float* p, const float (&x)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-}
-__device__ __forceinline__ void store4(bf16_t* p, const float (&x)[4]) {
-    uint2 v;
-    v.x = f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-    v.y = f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = v;
-}
 
 // float64 -> bf16 in one rounding (nearest, ties to even).  Normal range:
 // round the double's 52-bit fraction to bf16's 7 bits on the integer
@@ -90,142 +71,218 @@ __device__ __forceinline__ void rotate_store(bf16_t* p, int half, const float (&
 
 constexpr int kReorderThreads = 512;
 
-template <typename T>
+// Raw 4-element pieces as loaded (bf16 stays packed until it is used, so a
+// thread can hold more pieces in flight in the same registers).
+template <typename T> struct Piece;
+template <> struct Piece<float> {
+    using type = float4;
+    __device__ static type load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ static void unpack(const type& v, float (&x)[4]) { x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w; }
+    __device__ static void store(float* p, const type& v) { *reinterpret_cast<float4*>(p) = v; }
+};
+template <> struct Piece<bf16_t> {
+    using type = uint2;
+    __device__ static type load(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    __device__ static void unpack(const type& v, float (&x)[4]) {
+        x[0] = bf16_to_f32(v.x & 0xffffu); x[1] = bf16_to_f32(v.x >> 16);
+        x[2] = bf16_to_f32(v.y & 0xffffu); x[3] = bf16_to_f32(v.y >> 16);
+    }
+    __device__ static void store(bf16_t* p, const type& v) { *reinterpret_cast<uint2*>(p) = v; }
+};
+
+// SPW consecutive logical slots of one sequence per work-group: one for a
+// decode window (a few dozen slots: every slot gets its own work-group and
+// CU), four for the thousands of slots of a Dual-Stream pass (a quarter of
+// the work-groups, each with four times the loads in flight).
+template <typename T, int SPW>
 __global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderArgs a) {
-    const int i = blockIdx.x;   // logical slot
+    using P = Piece<T>;
+    const int i0 = blockIdx.x * SPW;   // first logical slot
     const int b = blockIdx.y;
     const int W = a.W, D = a.D, half = D / 2;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int ns = min(SPW, W - i0);   // slots of this work-group
 
     // Work items are 4 consecutive pairs (c .. c+3 with c+D/2 .. c+D/2+3) of
-    // one head: Hq query heads, then Hkv key heads; value rows are copied in
-    // 4-element pieces.
+    // one head of one slot: Hq query heads, then Hkv key heads; value rows
+    // are copied in 4-element pieces.
     const int qn = a.Hq * (half / 4), kn = a.Hkv * (half / 4), vn = a.Hkv * (D / 4);
     const int n_all = qn + kn + vn;
-    const T* qs = static_cast<const T*>(a.q) + ((size_t)b * W + i) * a.Hq * D;
-    const T* ks = static_cast<const T*>(a.k) + ((size_t)b * W + i) * a.Hkv * D;
-    const T* vs = static_cast<const T*>(a.v) + ((size_t)b * W + i) * a.Hkv * D;
+    const int n_tot = ns * n_all;
+    const size_t row_first = (size_t)b * W + i0;
 
-    // The rows of slot i depend on nothing else, so the first batch of
-    // kMaxItems items per thread is loaded before the permutation, the page
-    // and the angle table are known.  (Plain code, no lambdas: arrays
+    // The slots' rows depend on nothing else, so the first batch of
+    // kMaxItems items per thread is loaded before the permutation, the pages
+    // and the angle tables are known.  (Plain code, no lambdas: arrays
     // captured by a lambda were kept in scratch memory by the compiler.)
-    constexpr int kMaxItems = 2;
-    float x0[kMaxItems][4], x1[kMaxItems][4];
+    constexpr int kMaxItems = SPW == 1 ? 2 : 6;
+    typename P::type r0[kMaxItems], r1[kMaxItems];
 #pragma unroll
     for (int u = 0; u < kMaxItems; ++u) {
         const int it = tid + u * kReorderThreads;
-        if (it >= n_all) continue;
-        if (it < qn + kn) {
-            const bool isq = it < qn;
-            const int j = isq ? it : it - qn;
+        if (it >= n_tot) continue;
+        const int sl = it / n_all, jj = it - sl * n_all;
+        const size_t row = row_first + sl;
+        if (jj < qn + kn) {
+            const bool isq = jj < qn;
+            const int j = isq ? jj : jj - qn;
             const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-            const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
-            load4(src, x0[u]);
-            load4(src + half, x1[u]);
+            const T* src = isq ? static_cast<const T*>(a.q) + (row * a.Hq + hh) * D + c
+                               : static_cast<const T*>(a.k) + (row * a.Hkv + hh) * D + c;
+            r0[u] = P::load(src);
+            r1[u] = P::load(src + half);
         } else {
-            const int j = it - qn - kn;
-            load4(vs + (size_t)j * 4, x0[u]);
+            const int j = jj - qn - kn;
+            r0[u] = P::load(static_cast<const T*>(a.v) + row * a.Hkv * D + (size_t)j * 4);
         }
     }
 
-    // Every wave derives the physical row of slot i by itself from two
-    // ballots and a prefix popcount: no LDS, no barrier.
+    // Every wave derives the physical rows of its slots by itself from two
+    // ballots and prefix popcounts: slot i lands at r = popc(filled below i)
+    // if filled, else n_obs + popc(masked below i).  No LDS, no barrier.
     const bool in = lane < W;
     const int f = in ? a.filled[(size_t)b * W + lane] : 0;
     const int p_lane = in ? a.pos[(size_t)b * W + lane] : 0;
     const int L = a.ctx_len[b];
     const uint64_t fm = __ballot(in && f != 0);
     const uint64_t mm = __ballot(in && f == 0);
-    const uint64_t below = i == 0 ? 0ull : ((1ull << i) - 1ull);
     const int n_obs = __popcll(fm);
-    const int r = ((fm >> i) & 1ull) ? __popcll(fm & below) : n_obs + __popcll(mm & below);
-    const int p = __shfl(p_lane, i);
+    int rr[SPW], pp[SPW];
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl) {
+        const int i = min(i0 + sl, W - 1);
+        const uint64_t below = i == 0 ? 0ull : ((1ull << i) - 1ull);
+        rr[sl] = ((fm >> i) & 1ull) ? __popcll(fm & below) : n_obs + __popcll(mm & below);
+        pp[sl] = __shfl(p_lane, i);
+    }
 
-    // cos/sin of the D/2 pair angles, float64, once per work-group
-    __shared__ double s_cs[64], s_sn[64];
-    if (tid < half) {
+    // cos/sin of the D/2 pair angles of every slot, float64, once per
+    // work-group
+    __shared__ double s_cs[SPW][64], s_sn[SPW][64];
+    if (tid < ns * half) {
+        const int sl = tid / half, t = tid - sl * half;
+        int p = pp[0];
+#pragma unroll
+        for (int k = 1; k < SPW; ++k) p = sl == k ? pp[k] : p;
         double sn, cs;
-        sincos((double)p * exp2(-(2.0 * tid / D) * a.log2_base), &sn, &cs);
-        s_cs[tid] = cs;
-        s_sn[tid] = sn;
+        sincos((double)p * exp2(-(2.0 * t / D) * a.log2_base), &sn, &cs);
+        s_cs[sl][t] = cs;
+        s_sn[sl][t] = sn;
     }
 
     // The window's tokens L .. L+W-1 span at most W/16 + 2 pages: their
     // block-table entries are read as soon as L is known, one per lane.
     const bool ctx_ok = L >= 0 && (int64_t)L + W <= (int64_t)a.max_pages * kPage;
-    int page = -1;
+    size_t row0[SPW];     // cache row (page, head 0, offset) of each slot's token, or none
+    bool has_page[SPW];
+    bool bad_page = false;
     {
         const int fp = ctx_ok ? L / kPage : 0;
         const int npg = ctx_ok ? (L + W - 1) / kPage - fp + 1 : 0;
         const int pg_lane = lane < npg ? a.block_table[(size_t)b * a.max_pages + fp + lane] : -1;
-        if (ctx_ok) {
-            page = __shfl(pg_lane, (L + r) / kPage - fp);
-            if (page < 0 || page >= a.num_pages) page = -1;
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) {
+            int page = -1;
+            if (ctx_ok) {
+                page = __shfl(pg_lane, (L + rr[sl]) / kPage - fp);
+                if (page < 0 || page >= a.num_pages) page = -1;
+            }
+            has_page[sl] = page >= 0;
+            if (sl < ns && page < 0) bad_page = true;
+            const int t_row = L + rr[sl];
+            row0[sl] = page >= 0 ? ((size_t)page * a.Hkv) * kPage + (t_row % kPage) : 0;
         }
     }
-    if (tid == 0) {
-        a.perm[(size_t)b * W + r] = i;
-        if (!ctx_ok) set_status(a.status, WEDLM_DEV_BAD_CTX);
-        else if (page < 0) set_status(a.status, WEDLM_DEV_BAD_PAGE);
+    if (tid < ns) {
+        int r = rr[0];
+#pragma unroll
+        for (int k = 1; k < SPW; ++k) r = tid == k ? rr[k] : r;
+        a.perm[(size_t)b * W + r] = i0 + tid;
     }
-    if (tid < 64 && i == 0) {
+    if (tid == 0) {
+        if (!ctx_ok) set_status(a.status, WEDLM_DEV_BAD_CTX);
+        else if (bad_page) set_status(a.status, WEDLM_DEV_BAD_PAGE);
+    }
+    if (tid < 64 && i0 == 0) {
         const int p_prev = __shfl_up(p_lane, 1);
         const bool bad_pos = in && (p_lane < 0 || (lane > 0 && p_lane <= p_prev));
         if (__ballot(bad_pos) && lane == 0) set_status(a.status, WEDLM_DEV_BAD_POS);
     }
-    const int t_row = L + r;
-    const size_t row0 = page >= 0 ? ((size_t)page * a.Hkv) * kPage + (t_row % kPage) : 0;
-    T* qd = static_cast<T*>(a.q_phys) + ((size_t)b * W + r) * a.Hq * D;
     T* kc = static_cast<T*>(a.k_cache);
     T* vc = static_cast<T*>(a.v_cache);
     __syncthreads();
 
     // Every later batch loads all its items before using any.
-    for (int base = tid; base < n_all; base += kMaxItems * kReorderThreads) {
+    for (int base = tid; base < n_tot; base += kMaxItems * kReorderThreads) {
         if (base != tid)   // the first batch is already loaded
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
             const int it = base + u * kReorderThreads;
-            if (it >= n_all) continue;
-            if (it < qn + kn) {
-                const bool isq = it < qn;
-                const int j = isq ? it : it - qn;
+            if (it >= n_tot) continue;
+            const int sl = it / n_all, jj = it - sl * n_all;
+            const size_t row = row_first + sl;
+            if (jj < qn + kn) {
+                const bool isq = jj < qn;
+                const int j = isq ? jj : jj - qn;
                 const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-                const T* src = (isq ? qs : ks) + (size_t)hh * D + c;
-                load4(src, x0[u]);
-                load4(src + half, x1[u]);
+                const T* src = isq ? static_cast<const T*>(a.q) + (row * a.Hq + hh) * D + c
+                                   : static_cast<const T*>(a.k) + (row * a.Hkv + hh) * D + c;
+                r0[u] = P::load(src);
+                r1[u] = P::load(src + half);
             } else {
-                const int j = it - qn - kn;
-                load4(vs + (size_t)j * 4, x0[u]);
+                const int j = jj - qn - kn;
+                r0[u] = P::load(static_cast<const T*>(a.v) + row * a.Hkv * D + (size_t)j * 4);
             }
         }
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
             const int it = base + u * kReorderThreads;
-            if (it >= n_all || (it >= qn && page < 0)) continue;   // no cache row without a page
-            if (it < qn + kn) {
-                const bool isq = it < qn;
-                const int j = isq ? it : it - qn;
+            if (it >= n_tot) continue;
+            const int sl = it / n_all, jj = it - sl * n_all;
+            int r = rr[0];
+            size_t rw = row0[0];
+            bool hp = has_page[0];
+#pragma unroll
+            for (int k = 1; k < SPW; ++k) {
+                r = sl == k ? rr[k] : r;
+                rw = sl == k ? row0[k] : rw;
+                hp = sl == k ? has_page[k] : hp;
+            }
+            if (jj >= qn && !hp) continue;   // no cache row without a page
+            if (jj < qn + kn) {
+                const bool isq = jj < qn;
+                const int j = isq ? jj : jj - qn;
                 const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-                T* dst = isq ? qd + (size_t)hh * D + c : kc + (row0 + (size_t)hh * kPage) * D + c;
-                rotate_store(dst, half, x0[u], x1[u], s_cs + c, s_sn + c);
+                T* dst = isq ? static_cast<T*>(a.q_phys) + (((size_t)b * W + r) * a.Hq + hh) * D + c
+                             : kc + (rw + (size_t)hh * kPage) * D + c;
+                float x0[4], x1[4];
+                P::unpack(r0[u], x0);
+                P::unpack(r1[u], x1);
+                rotate_store(dst, half, x0, x1, &s_cs[sl][c], &s_sn[sl][c]);
             } else {
-                const int j = it - qn - kn;
+                const int j = jj - qn - kn;
                 const int g = j / (D / 4), d = (j % (D / 4)) * 4;
-                store4(vc + (row0 + (size_t)g * kPage) * D + d, x0[u]);
+                P::store(vc + (rw + (size_t)g * kPage) * D + d, r0[u]);
             }
         }
     }
 }
 
+// A Dual-Stream pass (thousands of slots) runs four slots per bf16
+// work-group; a decode window keeps one per slot.
+constexpr int kManySlots = 2048;
+
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream) {
-    dim3 grid(a.W, a.B), block(kReorderThreads);
-    if (dtype == WEDLM_F32)
-        hipLaunchKernelGGL(reorder_rope_append<float>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(reorder_rope_append<bf16_t>, grid, block, 0, stream, a);
+    dim3 block(kReorderThreads);
+    if (dtype == WEDLM_BF16 && (int64_t)a.B * a.W >= kManySlots) {
+        dim3 grid((a.W + 3) / 4, a.B);
+        hipLaunchKernelGGL((reorder_rope_append<bf16_t, 4>), grid, block, 0, stream, a);
+    } else if (dtype == WEDLM_F32) {
+        hipLaunchKernelGGL((reorder_rope_append<float, 1>), dim3(a.W, a.B), block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((reorder_rope_append<bf16_t, 1>), dim3(a.W, a.B), block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

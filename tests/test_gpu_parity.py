@@ -71,10 +71,17 @@ def _cfg(base_name, **kw):
     return wl.AttnConfig(**d)
 
 
+# A window of more than 2048 slots (B x W) takes the four-slots-per-work-
+# group launch of the reorder (the Dual-Stream pass's shape); W = 18 leaves
+# a two-slot tail group per sequence.
+MANY_SLOTS = _cfg("qwen3_l2048", name="many_slots_b128_w18", B=128, W=18, L=0, L_range=(0, 300), n_obs=None,
+                  seed=4711)
+
+
 # ---------------------------------------------------------------- reorder
-@pytest.mark.parametrize("name", ATTN_CFGS)
+@pytest.mark.parametrize("name", ATTN_CFGS + ["many_slots_b128_w18"])
 def test_reorder_parity(name, dev):
-    cfg = wl.CONFIGS[name]
+    cfg = MANY_SLOTS if name == MANY_SLOTS.name else wl.CONFIGS[name]
     print(f"[reorder] {name}", flush=True)
     inp = wl.make_attn_inputs(cfg)
     t = wl.device_attn_inputs(inp, dev)
