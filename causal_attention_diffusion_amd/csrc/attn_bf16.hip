@@ -123,6 +123,56 @@ __device__ __forceinline__ void tr_tile4(const uint32_t (&ad)[4], s16x4 (&r)[16]
           "=&v"(r[15])
         : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(8 * ROWB), "i"(16 * ROWB), "i"(24 * ROWB));
 }
+// The K fragments of one tile (8 ds_read_b128, D = 128) and the V
+// transpose reads of the previous tile (16 ds_read_b64_tr_b16) issued as one
+// batch: the asm returns once the K reads have landed (LDS reads of a wave
+// complete in order, so "at most 8 outstanding" after the first 8 V reads
+// means all K are in), with the V reads still in flight while the QK MFMAs
+// run; tr_wait16 waits for them before the PV MFMAs.  The V registers are
+// outputs here and read-write operands of tr_wait16, and nothing between the
+// two touches them (the compiler sees them as live values); no other LDS
+// read is issued in between, so the counts are exact.
+__device__ __forceinline__ void kv_issue(const uint32_t (&ka)[8], bf16x8 (&k)[8], const uint32_t (&ad)[4],
+                                         s16x4 (&r)[16]) {
+    asm volatile(
+        "ds_read_b128 %0, %24\n\t"
+        "ds_read_b128 %1, %25\n\t"
+        "ds_read_b128 %2, %26\n\t"
+        "ds_read_b128 %3, %27\n\t"
+        "ds_read_b128 %4, %28\n\t"
+        "ds_read_b128 %5, %29\n\t"
+        "ds_read_b128 %6, %30\n\t"
+        "ds_read_b128 %7, %31\n\t"
+        "ds_read_b64_tr_b16 %8, %32\n\t"
+        "ds_read_b64_tr_b16 %9, %33\n\t"
+        "ds_read_b64_tr_b16 %10, %34\n\t"
+        "ds_read_b64_tr_b16 %11, %35\n\t"
+        "ds_read_b64_tr_b16 %12, %32 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %13, %33 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %14, %34 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %15, %35 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(8)\n\t"
+        "ds_read_b64_tr_b16 %16, %32 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %17, %33 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %18, %34 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %19, %35 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %20, %32 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %21, %33 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %22, %34 offset:6144\n\t"
+        "ds_read_b64_tr_b16 %23, %35 offset:6144"
+        : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]),
+          "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
+          "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
+}
+__device__ __forceinline__ void tr_wait16(s16x4 (&r)[16]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]),
+                   "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]), "+v"(r[13]), "+v"(r[14]),
+                   "+v"(r[15]));
+}
 template <int ROWB>
 __device__ __forceinline__ void tr_tile2(const uint32_t (&ad)[2], s16x4 (&r)[8]) {
     asm volatile(
@@ -362,18 +412,15 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     };
 
     // S^T = K Q^T for this wave's tile of stage st, causal mask applied
-    auto qk = [&](int st, f32x16& sacc) {
-        const int key = tt_w * 32 + col;
-        const char* krow = kslot(st) + key * ROWB;
-        bf16x8 kf[D / 16];
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + swz_k(key, 2 * s + hl, C::RC) * 16);
+    auto qk_mfma = [&](const bf16x8 (&kf)[D / 16], f32x16& sacc) {
         f32x16 zero;
 #pragma unroll
         for (int e = 0; e < 16; ++e) zero[e] = 0.f;
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[0], zero, 0, 0, 0);
 #pragma unroll
         for (int s = 1; s < D / 16; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sacc, 0, 0, 0);
+    };
+    auto mask_tile = [&](int st, f32x16& sacc) {
         const int tb = k_begin + st * C::SK + tt_w * 32;   // first key of the tile
         if (tb + 31 > L) {        // uniform: only tiles reaching past the cached prefix
             asm volatile("");     // keep this a branch (no speculation into every tile)
@@ -381,6 +428,37 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 if ((e >> 2) * 8 + (e & 3) > thr) sacc[e] = -INFINITY;
+        }
+    };
+    auto qk = [&](int st, f32x16& sacc) {
+        const int key = tt_w * 32 + col;
+        const char* krow = kslot(st) + key * ROWB;
+        bf16x8 kf[D / 16];
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + swz_k(key, 2 * s + hl, C::RC) * 16);
+        qk_mfma(kf, sacc);
+        mask_tile(st, sacc);
+    };
+    // The same with the V reads of stage st - 1 in flight beside it (D = 128,
+    // one tile per wave and stage): kv_issue, then tr_wait16 before the PV.
+    uint32_t koff[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        const int key = tt_w * 32 + col;
+        koff[s] = (uint32_t)(key * ROWB + swz_k(key, 2 * s + hl, C::RC) * 16);
+    }
+    auto qk_v = [&](int st, f32x16& sacc) {
+        if constexpr (C::NDT == 4) {
+            const uint32_t kb = lds_u32(kslot(st)), vb = lds_u32(vslot(st - 1));
+            uint32_t ka[8], va[4];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) ka[s] = kb + koff[s];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) va[dt] = vb + vcol[dt];
+            bf16x8 kf[8];
+            kv_issue(ka, kf, va, vt);
+            qk_mfma(kf, sacc);
+            mask_tile(st, sacc);
         }
     };
 
@@ -458,18 +536,25 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     f32x16 sacc;
     bf16x8 pprev[2];
     if constexpr (PER == 1) {
-        // Every wave has a tile in every stage.  Iteration st: QK of st; then
-        // the 2*NDT PV MFMAs of st-1 interleaved with the softmax VALU work
-        // of st in one straight-line region, so each MFMA's pipe time covers
-        // a share of the softmax.
+        // Every wave has a tile in every stage.  Iteration st: QK of st (at
+        // D = 128 with the V reads of st-1 in flight); then the 2*NDT PV
+        // MFMAs of st-1 interleaved with the softmax VALU work of st in one
+        // straight-line region, so each MFMA's pipe time covers a share of
+        // the softmax.
         for (int st = 0; st < n_stages; ++st) {
             ring_step(st);
-            qk(st, sacc);
+            if constexpr (C::NDT == 4) {
+                if (st > 0) qk_v(st, sacc);
+                else qk(st, sacc);
+            } else {
+                qk(st, sacc);
+            }
             bf16x8 pn[2];
             float lsum;
             bool need;
             if (st > 0) {
-                pv_load(st - 1);
+                if constexpr (C::NDT == 4) tr_wait16(vt);
+                else pv_load(st - 1);
                 pv_mfma(pprev);
                 sm_core(sacc, pn, lsum, need);
 #pragma unroll
