@@ -30,6 +30,11 @@ using GemmSmall = TileCfg<256, 128, 64, 3, 4>;
 // outputs splits K at most 8 ways to fill the chip and the fp32 partials
 // stay small next to the weights
 using GemmRows = TileCfg<128, 256, 64, 3, 2>;
+// the plain projections at more rows: 256 output columns x 128 rows per
+// work-group, the row groups of one output tile on one XCD so the second
+// reads the weight tile from that XCD's L2 (the SwiGLU form keeps the
+// 256-row tile, whose epilogue pairs the gate and up columns)
+using GemmWide = TileCfg<256, 128, 64, 3, 4>;
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
 
@@ -230,7 +235,11 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmArgs& a, int m0, int t
 // P[s][m][n] = sum over the s-th K range of X[m][k] W[n][k], fp32, W the
 // stacked weight rows (or, in the SwiGLU form, the activation directly).  Work-group i: split s = i % S (so the work-groups of
 // one K range share an XCD when S divides 8 or 8 divides S), then row
-// group, then output tile.
+// group, then output tile.  On the 128-row tile with several row groups
+// the ids of one (output tile, split) unit's row groups lie 8 apart
+// (consecutive ids go round the 8 XCDs), so they share an XCD and its L2:
+// i = (u / 8 * nrg + mg) * 8 + u % 8 for unit u = nt * S + s, the grid
+// padded to whole groups of 8 units.
 template <class C>
 __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) char s_ring[C::SLOTS * C::SLOTB];
@@ -238,9 +247,19 @@ __global__ __launch_bounds__(64 * C::NW) void gemm_split(GemmArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int i = blockIdx.x;
-    const int s = i % a.S;
-    const int mg = (i / a.S) % a.nrg;
-    const int nt = i / a.S / a.nrg;
+    int s, mg, nt;
+    if (C::MT == 128 && a.nrg > 1) {
+        const int j = i >> 3;
+        mg = j % a.nrg;
+        const int u = (j / a.nrg) * 8 + (i & 7);
+        s = u % a.S;
+        nt = u / a.S;
+        if (nt * C::NT >= a.N) return;  // padding: the whole work-group leaves
+    } else {
+        s = i % a.S;
+        mg = (i / a.S) % a.nrg;
+        nt = i / a.S / a.nrg;
+    }
     const int m0 = mg * C::MT, n0 = nt * C::NT;
     if (tid < C::MT) s_rows[tid] = min(m0 + tid, a.M - 1);
     __syncthreads();
@@ -308,6 +327,11 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
         a.nrg = 1;
         const unsigned g = (unsigned)(((a.N + GemmSmall::NT - 1) / GemmSmall::NT) * a.S);
         hipLaunchKernelGGL(gemm_split<GemmSmall>, dim3(g), dim3(64 * GemmSmall::NW), 0, st, a);
+    } else if (!a.act) {
+        a.nrg = (a.M + GemmWide::MT - 1) / GemmWide::MT;
+        const unsigned units = (unsigned)(((a.N + GemmWide::NT - 1) / GemmWide::NT) * a.S);
+        const unsigned g = (units + 7) / 8 * 8 * (unsigned)a.nrg;
+        hipLaunchKernelGGL(gemm_split<GemmWide>, dim3(g), dim3(64 * GemmWide::NW), 0, st, a);
     } else {
         a.nrg = (a.M + GemmRows::MT - 1) / GemmRows::MT;
         const unsigned g = (unsigned)(((a.N + GemmRows::NT - 1) / GemmRows::NT) * a.nrg * a.S);
