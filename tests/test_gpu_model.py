@@ -72,11 +72,28 @@ def _rel(got, ref):
     return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
 
 
-def _run_stream(cfg, dev, steps, max_ctx):
+def _run_stream(cfg, dev, steps, max_ctx, prefix=0):
     w64, tw, handle, shape, ws, bt_t, bt = _setup(cfg, dev, max_ctx)
     B, W = cfg.B, cfg.W
-    tok, filled, pos, ctx = wl.initial_window(B, W, cfg.vocab)
+    tok, filled, pos, ctx = wl.initial_window(B, W, cfg.vocab, prefix)
     caches = [([np.zeros((0, cfg.Hkv, cfg.D))] * B, [np.zeros((0, cfg.Hkv, cfg.D))] * B) for _ in range(cfg.layers)]
+    if prefix:
+        # a cached prompt of `prefix` tokens per sequence in every layer:
+        # N(0,1) keys (taken as already rotated) and values in bf16, written to
+        # the shuffled pages on the GPU and handed to the oracle as its caches
+        rng = np.random.default_rng(cfg.seed + 29)
+        t = np.arange(prefix)
+        caches = []
+        for l in range(cfg.layers):
+            kv = []
+            for name in ("k_cache", "v_cache"):
+                bits = wl.to_storage(rng.standard_normal((B, prefix, cfg.Hkv, cfg.D)), "bf16")
+                host = tw["layers"][l][name].view(torch.int16).cpu().numpy().view(np.uint16)
+                for b in range(B):
+                    host[bt[b, t // PAGE], :, t % PAGE, :] = bits[b]
+                tw["layers"][l][name].copy_(torch.from_numpy(host.view(np.int16)).view(torch.bfloat16))
+                kv.append([wl.storage_to_f64(bits[b], "bf16") for b in range(B)])
+            caches.append((kv[0], kv[1]))
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     counters = torch.zeros((B, 2), dtype=torch.int64, device=dev)
     commits = []
@@ -134,6 +151,17 @@ def test_model_qwen3_layer_one_step(dev):
     # on a 4 x 64 window: 256 rows, split-K projections, two row tiles
     cfg = wl.MODEL_CONFIGS["model_qwen3_layer"]
     _run_stream(cfg, dev, 1, max_ctx=cfg.W)
+
+
+def test_model_qwen3_two_layers_stream(dev):
+    # two Qwen3-8B-shaped layers streamed for three steps on the 4 x 64
+    # window over a 512-token cached prompt: the second layer consumes the
+    # first's GPU output, and every step attends over the prompt and the
+    # rows the earlier steps committed
+    import dataclasses
+    cfg = dataclasses.replace(wl.MODEL_CONFIGS["model_qwen3_layer"], name="model_qwen3_2layers", layers=2)
+    ctx = _run_stream(cfg, dev, 3, max_ctx=512 + 3 * cfg.W, prefix=512)
+    assert (ctx > 512).all()
 
 
 @pytest.mark.parametrize("B,W", [(3, 48), (5, 64), (9, 64)])
