@@ -4,9 +4,12 @@
 A step is one pass of the whole decode path over one batch: wedlm_reorder
 (Topological Reordering + logical RoPE + KV append), wedlm_step_attn
 (windowed causal GQA attention over the paged prefix cache) and
-wedlm_select_commit (vocabulary confidence, commit, Eq. 11 fill, refill).
-Steps stream: each one commits tokens, so the context grows as it would in
-decoding.  Inputs are synthetic and resident in HBM before timing starts.
+wedlm_select_commit (vocabulary confidence, commit, Eq. 11 fill, refill),
+taken as one wedlm_decode_step call (the same three in three launches
+instead of five; --unfused times the three calls instead, and the line
+carries the other form's time beside it).  Steps stream: each one commits
+tokens, so the context grows as it would in decoding.  Inputs are synthetic
+and resident in HBM before timing starts.
 
 Default workload: batch 4, 32 Q / 8 KV heads, head dim 128, 32768 cached
 tokens in 16-token pages (shuffled), window 32 (16 observed), bf16; logits
@@ -82,6 +85,9 @@ def parse():
                     help="long_b4 only: skip the summaries of the other decode-step workloads and of the "
                          "select/commit workload that the default line carries under \"configs\"")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences in the CPU sample (0 = auto)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the step as the three calls (reorder, attention, select/commit) "
+                         "instead of one wedlm_decode_step")
     ap.add_argument("--eager", action="store_true",
                     help="time only eager launches (default: eager, then the same K steps replayed "
                          "as one captured HIP graph, which gives the reported value)")
@@ -185,7 +191,9 @@ def summarise_decode(r):
     """The figures of one decode-step workload kept in the headline line."""
     a = r["attn"]
     return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
-            "eager_ms_per_step": r["eager_ms_per_step"], "window_tokens_per_s": r["value"],
+            "eager_ms_per_step": r["eager_ms_per_step"], "step_call": r["step_call"],
+            **{k: r[k] for k in ("three_call_ms_per_step", "fused_ms_per_step") if k in r},
+            "window_tokens_per_s": r["value"],
             "steps_per_s": r["steps_per_s"], "split_kv": r["config"]["split_kv"],
             "attn": {"avg_ms": a["avg_ms"], "alg_bytes_per_launch": a["alg_bytes_per_launch"],
                      "GB_per_s": a["GB_per_s"], "frac_of_hbm_peak": r["roofline"]["frac"]},
@@ -195,7 +203,9 @@ def summarise_decode(r):
 
 def summarise_select(r):
     return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
-            "eager_ms_per_step": r["eager_ms_per_step"], "window_tokens_per_s": r["value"],
+            "eager_ms_per_step": r["eager_ms_per_step"], "step_call": r["step_call"],
+            **{k: r[k] for k in ("three_call_ms_per_step", "fused_ms_per_step") if k in r},
+            "window_tokens_per_s": r["value"],
             "select_commit": r["select_commit"], "frac_of_hbm_peak": r["roofline"]["frac"], "P_c": r["P_c"]}
 
 
@@ -249,11 +259,22 @@ def decode_leg(args, workload, with_cpu):
                                scfg.alpha, scfg.tau, mask_id, ws_sel, argmax_out=argmax_hist[i],
                                counters=counters)
 
-    def step(i):
+    def three_calls(i):
         reorder()
         attention()
         select(i)
 
+    # the same step as one wedlm_decode_step (three launches instead of five)
+    ws_step = wd.decode_step_workspace_tensor(t["q"], t["k_cache"], t["block_table"], max_ctx, args.vocab)
+
+    def fused(i):
+        wd.wedlm_decode_step(filled, pos, t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"], t["v_cache"],
+                             t["block_table"], ctx, t["perm"], t["out"], cfg.rope_base, max_ctx,
+                             logits[i % len(logits)], tok, n_commit_hist[i], committed, scfg.alpha, scfg.tau,
+                             mask_id, ws_step, argmax_out=argmax_hist[i], counters=counters,
+                             dev_status=t["status"])
+
+    step, other = (three_calls, fused) if args.unfused else (fused, three_calls)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -270,19 +291,21 @@ def decode_leg(args, workload, with_cpu):
             x.copy_(y)
         counters.zero_()
 
-    def eager_steps():
-        for i in range(args.warmup, total_steps):
-            step(i)
-
-    settle(eager_steps, restart)
-    restart()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    eager_steps()
-    torch.cuda.synchronize()
-    eager_elapsed = time.perf_counter() - t0
-    elapsed = eager_elapsed
-    if not args.eager:
+    def timed(fn):
+        """(eager seconds, replayed seconds or None) of K steps of fn from the
+        post-warm-up state; leaves the state the K steps produce."""
+        def eager_steps():
+            for i in range(args.warmup, total_steps):
+                fn(i)
+        settle(eager_steps, restart)
+        restart()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eager_steps()
+        torch.cuda.synchronize()
+        eager_s = time.perf_counter() - t0
+        if args.eager:
+            return eager_s, None
         state_eager = [x.clone() for x in (tok, filled, pos, ctx, counters)]
         restart()
         graph = capture_steps(eager_steps)
@@ -292,11 +315,24 @@ def decode_leg(args, workload, with_cpu):
         t0 = time.perf_counter()
         graph.launch()
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        replay_s = time.perf_counter() - t0
         for x, y in zip((tok, filled, pos, ctx, counters), state_eager):
             if not torch.equal(x, y):
                 print("graph replay diverged from the eager steps", file=sys.stderr)
                 sys.exit(3)
+        return eager_s, replay_s
+
+    # the other form of the step first (for comparison), then the measured one;
+    # both must leave the same state
+    other_eager, other_replay = timed(other)
+    state_other = [x.clone() for x in (tok, filled, pos, ctx, counters, n_commit_hist, t["out"])]
+    eager_elapsed, replay_elapsed = timed(step)
+    elapsed = eager_elapsed if replay_elapsed is None else replay_elapsed
+    for x, y in zip((tok, filled, pos, ctx, counters, n_commit_hist, t["out"]), state_other):
+        if not torch.equal(x, y):
+            print("wedlm_decode_step and the three calls diverged", file=sys.stderr)
+            sys.exit(3)
+    other_elapsed = other_eager if other_replay is None else other_replay
     cnt = counters.cpu().numpy()
 
     # ---- timed region 2: the attention call alone, K launches back to back on
@@ -395,7 +431,9 @@ def decode_leg(args, workload, with_cpu):
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
         "graph": not args.eager,
+        "step_call": "wedlm_reorder + wedlm_step_attn + wedlm_select_commit" if args.unfused else "wedlm_decode_step",
         "eager_ms_per_step": round(eager_elapsed * 1e3 / args.steps, 4),
+        ("fused_ms_per_step" if args.unfused else "three_call_ms_per_step"): round(other_elapsed * 1e3 / args.steps, 4),
         "config": {"workload": f"{cfg.name}: B={B} W={W} Hq={Hq} Hkv={Hkv} D={D} "
                                f"prefix={int(inp.ctx_len.max()) if cfg.L_range is None else str(cfg.L_range)} "
                                f"page=16 vocab={args.vocab} streaming decode step (reorder+attn+select/commit)",
@@ -426,7 +464,7 @@ def decode_leg(args, workload, with_cpu):
 
     if with_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg, args, inp)
-    del t, ws_attn, ws_sel, logits
+    del t, ws_attn, ws_sel, ws_step, logits
     torch.cuda.empty_cache()
     return result
 

@@ -12,6 +12,8 @@ if the library is not built, every call raises.
                        out, max_ctx_len=..., workspace=ws)
     wd.wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit,
                            committed, alpha=..., tau=..., mask_id=..., workspace=ws2)
+
+or the same three as one call with fewer launches, ``wd.wedlm_decode_step``.
 """
 from .binding import (  # noqa: F401
     WEDLM_BF16,
@@ -28,7 +30,10 @@ from .binding import (  # noqa: F401
     make_shape,
     select_workspace_tensor,
     attn_workspace_tensor,
+    decode_step_workspace_tensor,
     dual_stream_workspace_tensor,
+    wedlm_decode_step,
+    wedlm_decode_step_workspace,
     wedlm_dual_stream_attn,
     wedlm_attn_plan,
     wedlm_last_error,

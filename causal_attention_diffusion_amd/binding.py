@@ -31,6 +31,16 @@ class WedlmShape(C.Structure):
 LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down", "k_cache", "v_cache")
 
 
+class WedlmStepIO(C.Structure):
+    """wedlm_step_io: the pointers and scalars of one wedlm_decode_step."""
+    _fields_ = [(n, C.c_void_p) for n in ("tok", "filled", "pos", "ctx_len", "q", "k", "v", "logits",
+                                          "k_cache", "v_cache", "block_table", "q_phys", "perm", "out",
+                                          "n_commit", "committed", "argmax_out", "entropy_out", "counters",
+                                          "dev_status")] + \
+               [("V", C.c_int32), ("max_ctx_len", C.c_int32), ("mask_id", C.c_int32), ("scale", C.c_float),
+                ("alpha", C.c_float), ("tau", C.c_float), ("rope_base", C.c_double)]
+
+
 class WedlmLayerWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in LAYER_FIELDS]
 
@@ -71,6 +81,10 @@ def load_library():
     lib.wedlm_select_commit.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
                                         C.c_float, C.c_float, i32, P, sz, P]
     lib.wedlm_select_commit.restype = C.c_int
+    lib.wedlm_decode_step_workspace.argtypes = [S, i32, i32]
+    lib.wedlm_decode_step_workspace.restype = sz
+    lib.wedlm_decode_step.argtypes = [S, C.POINTER(WedlmStepIO), P, sz, P]
+    lib.wedlm_decode_step.restype = C.c_int
     lib.wedlm_lmhead_select_commit_workspace.argtypes = [i32, i32, i32, i32]
     lib.wedlm_lmhead_select_commit_workspace.restype = sz
     lib.wedlm_lmhead_select_commit.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P,
@@ -301,6 +315,61 @@ def wedlm_select_commit(logits, tok, filled, pos, ctx_len, n_commit, committed, 
         B, W, V, _ptr(logits), _ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len), _ptr(n_commit),
         _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(counters), float(alpha), float(tau),
         int(mask_id), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def wedlm_decode_step_workspace(q, k_cache, block_table, max_ctx_len: int, V: int) -> int:
+    s = _shape_from(q, k_cache, block_table)
+    return int(load_library().wedlm_decode_step_workspace(C.byref(s), int(max_ctx_len), int(V)))
+
+
+def decode_step_workspace_tensor(q, k_cache, block_table, max_ctx_len: int, V: int):
+    """Workspace for wedlm_decode_step (no initialisation needed)."""
+    import torch
+    n = wedlm_decode_step_workspace(q, k_cache, block_table, max_ctx_len, V)
+    if n == 0:
+        raise WedlmError(f"unsupported decode-step shape (max_ctx_len={max_ctx_len}, V={V})")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def wedlm_decode_step(filled, pos, q, k, v, q_phys, k_cache, v_cache, block_table, ctx_len, perm, out,
+                      rope_base: float, max_ctx_len: int, logits, tok, n_commit, committed, alpha: float,
+                      tau: float, mask_id: int, workspace, scale: float = 0.0, argmax_out=None,
+                      entropy_out=None, counters=None, dev_status=None, stream=None):
+    """One whole decode step: the arguments of wedlm_reorder, wedlm_step_attn and
+    wedlm_select_commit (same names), run as one call with fewer launches."""
+    import torch
+    s = _shape_from(q, k_cache, block_table)
+    B, W, Hq, Hkv, D = s.B, s.W, s.Hq, s.Hkv, s.D
+    _expect(filled, "filled", (B, W), torch.uint8)
+    _expect(pos, "pos", (B, W), torch.int32)
+    _expect(k, "k", (B, W, Hkv, D), q.dtype)
+    _expect(v, "v", (B, W, Hkv, D), q.dtype)
+    _expect(q_phys, "q_phys", tuple(q.shape), q.dtype)
+    _expect(k_cache, "k_cache", tuple(k_cache.shape), q.dtype)
+    _expect(v_cache, "v_cache", tuple(k_cache.shape), q.dtype)
+    _expect(block_table, "block_table", tuple(block_table.shape), torch.int32)
+    _expect(ctx_len, "ctx_len", (B,), torch.int32)
+    _expect(perm, "perm", (B, W), torch.int32)
+    _expect(out, "out", (B, W, Hq, D), q.dtype)
+    if logits is None or logits.dim() != 3 or logits.dtype != torch.float32 or tuple(logits.shape[:2]) != (B, W):
+        raise WedlmError(f"logits must be a [{B}, {W}, V] float32 tensor")
+    V = logits.shape[2]
+    _expect(tok, "tok", (B, W), torch.int32)
+    _expect(n_commit, "n_commit", (B,), torch.int32)
+    _expect(committed, "committed", (B, W), torch.int32)
+    _opt(argmax_out, "argmax_out", (B, W), torch.int32)
+    _opt(entropy_out, "entropy_out", (B, W), torch.float32)
+    _opt(counters, "counters", (B, 2), torch.int64)
+    _opt(dev_status, "dev_status", (1,), torch.int32)
+    if workspace is None or workspace.dtype != torch.uint8:
+        raise WedlmError("workspace must be a uint8 tensor (decode_step_workspace_tensor)")
+    io = WedlmStepIO(_ptr(tok), _ptr(filled), _ptr(pos), _ptr(ctx_len), _ptr(q), _ptr(k), _ptr(v), _ptr(logits),
+                     _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(q_phys), _ptr(perm), _ptr(out),
+                     _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(counters),
+                     _ptr(dev_status), int(V), int(max_ctx_len), int(mask_id), float(scale), float(alpha),
+                     float(tau), float(rope_base))
+    _check(load_library().wedlm_decode_step(C.byref(s), C.byref(io), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def wedlm_lmhead_select_commit_workspace(B: int, W: int, V: int, Dm: int) -> int:

@@ -58,22 +58,33 @@ static int check_shape(const wedlm_shape* s) {
     return WEDLM_OK;
 }
 
-extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const int32_t* pos, const void* q,
-                             const void* k, const void* v, void* q_phys, void* k_cache, void* v_cache,
-                             const int32_t* block_table, const int32_t* ctx_len, int32_t* perm,
-                             double rope_base, int32_t* dev_status, void* stream) {
+// Checks of wedlm_reorder's arguments and its kernel argument block.
+static int reorder_args(const wedlm_shape* s, const uint8_t* filled, const int32_t* pos, const void* q,
+                        const void* k, const void* v, void* q_phys, void* k_cache, void* v_cache,
+                        const int32_t* block_table, const int32_t* ctx_len, int32_t* perm, double rope_base,
+                        int32_t* dev_status, ReorderArgs* a) {
     int rc = check_shape(s);
     if (rc) return rc;
     if (!filled || !pos || !q || !k || !v || !q_phys || !k_cache || !v_cache || !block_table || !ctx_len || !perm)
         return fail(WEDLM_ERR_ARG, "wedlm_reorder: NULL device pointer");
     if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(WEDLM_ERR_ARG, "rope_base must be > 1");
+    a->filled = filled; a->pos = pos; a->q = q; a->k = k; a->v = v; a->q_phys = q_phys;
+    a->k_cache = k_cache; a->v_cache = v_cache; a->block_table = block_table; a->ctx_len = ctx_len;
+    a->perm = perm; a->status = dev_status;
+    a->B = s->B; a->W = s->W; a->Hq = s->Hq; a->Hkv = s->Hkv; a->D = s->D;
+    a->max_pages = s->max_pages; a->num_pages = s->num_pages;
+    a->log2_base = log2(rope_base);
+    return WEDLM_OK;
+}
+
+extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const int32_t* pos, const void* q,
+                             const void* k, const void* v, void* q_phys, void* k_cache, void* v_cache,
+                             const int32_t* block_table, const int32_t* ctx_len, int32_t* perm,
+                             double rope_base, int32_t* dev_status, void* stream) {
     ReorderArgs a;
-    a.filled = filled; a.pos = pos; a.q = q; a.k = k; a.v = v; a.q_phys = q_phys;
-    a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table; a.ctx_len = ctx_len;
-    a.perm = perm; a.status = dev_status;
-    a.B = s->B; a.W = s->W; a.Hq = s->Hq; a.Hkv = s->Hkv; a.D = s->D;
-    a.max_pages = s->max_pages; a.num_pages = s->num_pages;
-    a.log2_base = log2(rope_base);
+    const int rc = reorder_args(s, filled, pos, q, k, v, q_phys, k_cache, v_cache, block_table, ctx_len, perm,
+                                rope_base, dev_status, &a);
+    if (rc) return rc;
     return hip_status(launch_reorder(a, s->dtype, (hipStream_t)stream), "wedlm_reorder launch");
 }
 
@@ -552,9 +563,12 @@ extern "C" int wedlm_step_attn_noalloc(const wedlm_shape* s, const void* q_phys,
                      dev_status, stream);
 }
 
-static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
+// Checks of wedlm_step_attn's arguments, its plan and its kernel argument
+// block.
+static int attn_args(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* ctx_len, const int32_t* perm, void* out, float scale,
-                     int32_t max_ctx_len, void* workspace, size_t ws_bytes, int32_t* dev_status, void* stream) {
+                     int32_t max_ctx_len, void* workspace, size_t ws_bytes, int32_t* dev_status, AttnArgs* ap,
+                     Plan* pp) {
     int rc = check_shape(s);
     if (rc) return rc;
     if (!q_phys || !k_cache || !v_cache || !block_table || !ctx_len || !perm || !out)
@@ -568,7 +582,7 @@ static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cac
     Plan p = make_plan(s, max_ctx_len);
     if (p.ws_bytes > 0 && (!workspace || ws_bytes < p.ws_bytes))
         return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", p.ws_bytes, workspace ? ws_bytes : 0);
-    AttnArgs a;
+    AttnArgs& a = *ap;
     a.q = q_phys; a.k_cache = k_cache; a.v_cache = v_cache; a.block_table = block_table;
     a.ctx_len = ctx_len; a.perm = perm; a.out = out;
     a.part_o = static_cast<float*>(workspace);
@@ -581,6 +595,18 @@ static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cac
     a.max_ctx = max_ctx_len;
     const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)s->D);
     a.scale_log2 = sc * kLog2e;
+    *pp = p;
+    return WEDLM_OK;
+}
+
+static int step_attn(const wedlm_shape* s, const void* q_phys, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* ctx_len, const int32_t* perm, void* out, float scale,
+                     int32_t max_ctx_len, void* workspace, size_t ws_bytes, int32_t* dev_status, void* stream) {
+    AttnArgs a;
+    Plan p;
+    const int rc = attn_args(s, q_phys, k_cache, v_cache, block_table, ctx_len, perm, out, scale, max_ctx_len,
+                             workspace, ws_bytes, dev_status, &a, &p);
+    if (rc) return rc;
     return hip_status(launch_attn(a, s->dtype, s->D, p.nw, (hipStream_t)stream), "wedlm_step_attn launch");
 }
 
@@ -620,11 +646,11 @@ extern "C" size_t wedlm_select_commit_workspace(int32_t B, int32_t W, int32_t V)
     return ((size_t)B * W * np * sizeof(float4) + 255) / 256 * 256;
 }
 
-extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float* logits, int32_t* tok,
-                                   uint8_t* filled, int32_t* pos, int32_t* ctx_len, int32_t* n_commit,
-                                   int32_t* committed, int32_t* argmax_out, float* entropy_out, int64_t* counters,
-                                   float alpha, float tau, int32_t mask_id, void* workspace, size_t ws_bytes,
-                                   void* stream) {
+// Checks of wedlm_select_commit's arguments and its kernel argument block.
+static int select_args(int32_t B, int32_t W, int32_t V, const float* logits, int32_t* tok, uint8_t* filled,
+                       int32_t* pos, int32_t* ctx_len, int32_t* n_commit, int32_t* committed, int32_t* argmax_out,
+                       float* entropy_out, int64_t* counters, float alpha, float tau, int32_t mask_id,
+                       void* workspace, size_t ws_bytes, SelectArgs* ap) {
     if (B < 1 || W < 1 || W > 64 || V < 1)
         return fail(WEDLM_ERR_SHAPE, "need B >= 1, 1 <= W <= 64, V >= 1 (B=%d W=%d V=%d)", B, W, V);
     int np, pl;
@@ -638,14 +664,81 @@ extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float*
     const size_t need = wedlm_select_commit_workspace(B, W, V);
     if (!workspace || ws_bytes < need)
         return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : 0);
-    SelectArgs a;
+    SelectArgs& a = *ap;
     a.logits = logits; a.tok = tok; a.filled = filled; a.pos = pos; a.ctx_len = ctx_len;
     a.n_commit = n_commit; a.committed = committed; a.argmax_out = argmax_out; a.entropy_out = entropy_out;
     a.counters = counters;
     a.part = static_cast<float4*>(workspace);
     a.B = B; a.W = W; a.V = V; a.nparts = np; a.part_len = pl;
     a.alpha = alpha; a.tau = tau; a.mask_id = mask_id;
+    return WEDLM_OK;
+}
+
+extern "C" int wedlm_select_commit(int32_t B, int32_t W, int32_t V, const float* logits, int32_t* tok,
+                                   uint8_t* filled, int32_t* pos, int32_t* ctx_len, int32_t* n_commit,
+                                   int32_t* committed, int32_t* argmax_out, float* entropy_out, int64_t* counters,
+                                   float alpha, float tau, int32_t mask_id, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+    SelectArgs a;
+    const int rc = select_args(B, W, V, logits, tok, filled, pos, ctx_len, n_commit, committed, argmax_out,
+                               entropy_out, counters, alpha, tau, mask_id, workspace, ws_bytes, &a);
+    if (rc) return rc;
     return hip_status(launch_select(a, (hipStream_t)stream), "wedlm_select_commit launch");
+}
+
+// ---------------------------------------------------------------- whole decode step
+// Workspace of wedlm_decode_step: the attention's split partials, then the
+// vocabulary partials, each on a 256-byte boundary.
+static size_t step_attn_bytes(const wedlm_shape* s, int32_t max_ctx_len) {
+    return (make_plan(s, max_ctx_len).ws_bytes + 255) / 256 * 256;
+}
+
+extern "C" size_t wedlm_decode_step_workspace(const wedlm_shape* s, int32_t max_ctx_len, int32_t V) {
+    if (check_shape(s) || max_ctx_len < 0 || (int64_t)max_ctx_len + s->W > kMaxContext) return 0;
+    const size_t sel = wedlm_select_commit_workspace(s->B, s->W, V);
+    return sel ? step_attn_bytes(s, max_ctx_len) + sel : 0;
+}
+
+extern "C" int wedlm_decode_step(const wedlm_shape* s, const wedlm_step_io* io, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    if (!io) return fail(WEDLM_ERR_ARG, "wedlm_decode_step: io is NULL");
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (io->max_ctx_len < 0) return fail(WEDLM_ERR_ARG, "max_ctx_len must be >= 0");
+    if ((int64_t)io->max_ctx_len + s->W > kMaxContext)
+        return fail(WEDLM_ERR_UNSUPPORTED, "context of %lld tokens: built for up to %lld",
+                    (long long)io->max_ctx_len + s->W, (long long)kMaxContext);
+    const size_t need = wedlm_decode_step_workspace(s, io->max_ctx_len, io->V);
+    if (need == 0) return fail(WEDLM_ERR_SHAPE, "need V >= 1 (V=%d)", io->V);
+    if (!workspace || ws_bytes < need)
+        return fail(WEDLM_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? ws_bytes : 0);
+    char* ws = static_cast<char*>(workspace);
+    const size_t attn_bytes = step_attn_bytes(s, io->max_ctx_len);
+    ReorderArgs ra;
+    AttnArgs aa;
+    Plan p;
+    SelectArgs sa;
+    if ((rc = reorder_args(s, io->filled, io->pos, io->q, io->k, io->v, io->q_phys, io->k_cache, io->v_cache,
+                           io->block_table, io->ctx_len, io->perm, io->rope_base, io->dev_status, &ra)))
+        return rc;
+    if ((rc = attn_args(s, io->q_phys, io->k_cache, io->v_cache, io->block_table, io->ctx_len, io->perm, io->out,
+                        io->scale, io->max_ctx_len, attn_bytes ? ws : nullptr, attn_bytes, io->dev_status, &aa,
+                        &p)))
+        return rc;
+    if ((rc = select_args(s->B, s->W, io->V, io->logits, io->tok, io->filled, io->pos, io->ctx_len, io->n_commit,
+                          io->committed, io->argmax_out, io->entropy_out, io->counters, io->alpha, io->tau,
+                          io->mask_id, ws + attn_bytes, ws_bytes - attn_bytes, &sa)))
+        return rc;
+    // the front launch is one-dimensional with 512 work-items per work-group
+    // (one per slot, then two vocabulary units each): its work-item count
+    // must fit the dispatch's 32 bits
+    if ((int64_t)s->B * s->W + ((int64_t)s->B * s->W * sa.nparts + 1) / 2 >= (1ll << 23))
+        return fail(WEDLM_ERR_SHAPE, "wedlm_decode_step: grid too large (B=%d W=%d parts=%d)", s->B, s->W, sa.nparts);
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = hip_status(launch_step_front(ra, sa, s->dtype, st), "wedlm_decode_step front launch"))) return rc;
+    if ((rc = hip_status(launch_attn_split(aa, s->dtype, s->D, p.nw, st), "wedlm_decode_step attention launch")))
+        return rc;
+    return hip_status(launch_step_back(aa, sa, s->dtype, s->D, st), "wedlm_decode_step back launch");
 }
 
 // ---------------------------------------------------------------- graph capture

@@ -32,7 +32,7 @@
 //
 // The bf16 kernels (attn_bf16.hip) use the same transposed tiling with
 // direct global-to-LDS loads.
-#include "kernels.hpp"
+#include "select.hpp"
 
 namespace wedlm {
 
@@ -90,7 +90,14 @@ __global__ __launch_bounds__(64 * NW) void attn_split_f32(AttnArgs a) {
     const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
     const int k_begin = split * sk;
     const int k_end = min(T_len, k_begin + sk);
-    if (k_begin >= k_end && a.nsplit > 1) return;  // merged away by attn_combine
+    if (k_begin >= k_end && a.nsplit > 1) {
+        // no key here: the split's rows get an empty partial (m = -inf, l = 0),
+        // which attn_combine weighs zero without reading its O
+        const size_t prow0 = ((size_t)pid * a.nsplit + split) * C::RT;
+        for (int i = tid; i < C::RT; i += C::NT)
+            if (rt * C::RT + i < a.M) a.part_ml[prow0 + i] = make_float2(-INFINITY, 0.f);
+        return;
+    }
 
     // block-table slice of this split
     const int p0 = k_begin / kPage;
@@ -277,14 +284,13 @@ __global__ __launch_bounds__(64 * NW) void attn_split_f32(AttnArgs a) {
 // so one memory latency covers a batch (the D/4 threads of a row read the
 // same (m, l) words: one request per wave).  No LDS, no barrier.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+__device__ __forceinline__ void combine_rows(const AttnArgs& a, int blk, int tid) {
     constexpr int D4 = D / 4;
     constexpr int RPB = 256 / D4;
     constexpr int SB = 8;                      // splits per batch
-    const int tid = threadIdx.x;
     const int lr = tid / D4;
     const int d = (tid % D4) * 4;
-    const long row = (long)blockIdx.x * RPB + lr;
+    const long row = (long)blk * RPB + lr;
     const int npid = a.B * a.Hkv * a.row_tiles;
     const int pid = (int)(row / a.RT);
     if (pid >= npid) return;
@@ -295,24 +301,19 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     const int b = bk / a.Hkv;
     const int m = rt * a.RT + m_loc;
     if (m >= a.M) return;
-    const int L = a.ctx_len[b];
-    const bool ctx_ok = L >= 0 && L <= a.max_ctx && (int64_t)L + a.W <= (int64_t)a.max_pages * kPage;
-    const int T_len = ctx_ok ? L + a.W : 0;
-    const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
-    const int nvalid = min(a.nsplit, (T_len + sk - 1) / sk);
     const size_t base = (size_t)pid * a.nsplit * a.RT + m_loc;
     const float* po = a.part_o + base * D + d;
     const size_t stride = (size_t)a.RT * D;
 
     float M = -INFINITY, den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < nvalid; s0 += SB) {
+    for (int s0 = 0; s0 < a.nsplit; s0 += SB) {
         float2 ml[SB];
         float4 v[SB];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
             const int s = s0 + j;
-            if (s < nvalid) {
+            if (s < a.nsplit) {
                 ml[j] = a.part_ml[base + (size_t)s * a.RT];
                 v[j] = *reinterpret_cast<const float4*>(po + s * stride);
             } else {
@@ -320,6 +321,11 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
                 v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
+        // a split without keys left its O unwritten (m = -inf): weigh it zero
+        // by selection, whatever the workspace holds there
+#pragma unroll
+        for (int j = 0; j < SB; ++j)
+            if (ml[j].x == -INFINITY) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         float Mb = M;
 #pragma unroll
         for (int j = 0; j < SB; ++j) Mb = fmaxf(Mb, ml[j].x);
@@ -355,11 +361,42 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 }
 
 template <typename T, int D>
-static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+    combine_rows<T, D>(a, blockIdx.x, threadIdx.x);
+}
+
+// Back half of a fused decode step: the commit / Eq. 11 select / refill of
+// every sequence (one wave each, four per work-group, first) and the
+// combine's work-groups in one launch.  They touch disjoint memory: the
+// combine reads the split partials and perm and writes out; the commit reads
+// the vocabulary partials and rewrites the window state and ctx_len, which
+// the combine does not read.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void step_back(AttnArgs a, SelectArgs s, int n_commit_blocks) {
+    const int blk = blockIdx.x;
+    if (blk < n_commit_blocks) {
+        const int b = blk * 4 + (int)(threadIdx.x >> 6);
+        if (b < s.B) commit_seq(s, b, threadIdx.x & 63);
+    } else {
+        combine_rows<T, D>(a, blk - n_commit_blocks, threadIdx.x);
+    }
+}
+
+template <int D>
+static unsigned combine_blocks(const AttnArgs& a) {
     constexpr int RPB = 256 / (D / 4);
     const long rows = (long)a.B * a.Hkv * a.row_tiles * a.RT;
-    dim3 g2((unsigned)((rows + RPB - 1) / RPB)), b2(256);
-    hipLaunchKernelGGL((attn_combine<T, D>), g2, b2, 0, st, a);
+    return (unsigned)((rows + RPB - 1) / RPB);
+}
+template <typename T, int D>
+static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL((attn_combine<T, D>), dim3(combine_blocks<D>(a)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+template <typename T, int D>
+static hipError_t launch_step_back_t(const AttnArgs& a, const SelectArgs& s, hipStream_t st) {
+    const int nc = (s.B + 3) / 4;
+    hipLaunchKernelGGL((step_back<T, D>), dim3(combine_blocks<D>(a) + (unsigned)nc), dim3(256), 0, st, a, s, nc);
     return hipGetLastError();
 }
 
@@ -374,17 +411,25 @@ int attn_chunk(int dtype, int nw) { return dtype == WEDLM_BF16 ? 64 : 32; }
 
 hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st);
 
-hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {
-    hipError_t e;
+hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {
     if (dtype == WEDLM_F32) {
-        if (D == 64) e = nw == 1 ? launch_f32_t<64, 1>(a, st) : nw == 2 ? launch_f32_t<64, 2>(a, st) : launch_f32_t<64, 4>(a, st);
-        else e = nw == 1 ? launch_f32_t<128, 1>(a, st) : nw == 2 ? launch_f32_t<128, 2>(a, st) : launch_f32_t<128, 4>(a, st);
-    } else {
-        e = launch_attn_bf16_split(a, D, nw, st);
+        if (D == 64) return nw == 1 ? launch_f32_t<64, 1>(a, st) : nw == 2 ? launch_f32_t<64, 2>(a, st) : launch_f32_t<64, 4>(a, st);
+        return nw == 1 ? launch_f32_t<128, 1>(a, st) : nw == 2 ? launch_f32_t<128, 2>(a, st) : launch_f32_t<128, 4>(a, st);
     }
+    return launch_attn_bf16_split(a, D, nw, st);
+}
+
+hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {
+    const hipError_t e = launch_attn_split(a, dtype, D, nw, st);
     if (e != hipSuccess || a.nsplit == 1) return e;
     if (dtype == WEDLM_F32) return D == 64 ? launch_combine_t<float, 64>(a, st) : launch_combine_t<float, 128>(a, st);
     return D == 64 ? launch_combine_t<bf16_t, 64>(a, st) : launch_combine_t<bf16_t, 128>(a, st);
+}
+
+hipError_t launch_step_back(const AttnArgs& a, const SelectArgs& s, int dtype, int D, hipStream_t st) {
+    if (a.nsplit == 1) return launch_commit(s, st);
+    if (dtype == WEDLM_F32) return D == 64 ? launch_step_back_t<float, 64>(a, s, st) : launch_step_back_t<float, 128>(a, s, st);
+    return D == 64 ? launch_step_back_t<bf16_t, 64>(a, s, st) : launch_step_back_t<bf16_t, 128>(a, s, st);
 }
 
 }  // namespace wedlm

@@ -262,7 +262,14 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
     const int k_begin = split * sk;
     const int k_end = min(T_len, k_begin + sk);
-    if (k_begin >= k_end && a.nsplit > 1) return;  // nothing here; attn_combine skips this split
+    if (k_begin >= k_end && a.nsplit > 1) {
+        // no key here: the split's rows get an empty partial (m = -inf, l = 0),
+        // which attn_combine weighs zero without reading its O
+        const size_t prow0 = ((size_t)pid * a.nsplit + split) * RT;
+        for (int i = tid; i < RT; i += C::NT)
+            if (rt * RT + i < a.M) a.part_ml[prow0 + i] = make_float2(-INFINITY, 0.f);
+        return;
+    }
 
     const int p0 = k_begin / kPage;
     const int np = k_end > k_begin ? (k_end + kPage - 1) / kPage - p0 : 0;

@@ -88,6 +88,8 @@ __device__ __forceinline__ int split_len(int T_len, int nsplit, int split_keys, 
 
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
+// the split kernel alone (no combine)
+hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
 int attn_chunk(int dtype, int nw);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 struct ModelRowArgs {
@@ -132,5 +134,10 @@ hipError_t launch_dual_layout(uint8_t* filled_m, int32_t* pos_m, int32_t* ctx_m,
                               int32_t* ctx_p, int32_t* bt_p, int S, int N, int b, hipStream_t stream);
 // commit / Eq. 11 select / refill alone, on row partials already in a.part
 hipError_t launch_commit(const SelectArgs& a, hipStream_t stream);
+// Fused decode step: the reorder with the vocabulary pass, then (after the
+// split kernel) the combine with the commit (the commit alone when the
+// plan has one split).
+hipError_t launch_step_front(const ReorderArgs& r, const SelectArgs& s, int dtype, hipStream_t stream);
+hipError_t launch_step_back(const AttnArgs& a, const SelectArgs& s, int dtype, int D, hipStream_t stream);
 
 }  // namespace wedlm

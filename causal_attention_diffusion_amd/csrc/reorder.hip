@@ -18,7 +18,7 @@
 // cache at token ctx_len[b] + r.
 // The work is tiny (B*W*(Hq+2Hkv)*D elements) and latency-bound; angles and
 // rotations are float64 so that positions up to 2^31 keep full accuracy.
-#include "kernels.hpp"
+#include "select.hpp"
 
 namespace wedlm {
 
@@ -95,10 +95,9 @@ template <> struct Piece<bf16_t> {
 // CU), four for the thousands of slots of a Dual-Stream pass (a quarter of
 // the work-groups, each with four times the loads in flight).
 template <typename T, int SPW>
-__global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderArgs a) {
+__device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int b) {
     using P = Piece<T>;
-    const int i0 = blockIdx.x * SPW;   // first logical slot
-    const int b = blockIdx.y;
+    const int i0 = bx * SPW;           // first logical slot
     const int W = a.W, D = a.D, half = D / 2;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -269,13 +268,43 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderAr
     }
 }
 
+template <typename T, int SPW>
+__global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderArgs a) {
+    reorder_slots<T, SPW>(a, blockIdx.x, blockIdx.y);
+}
+
+// Front half of a fused decode step: the reorder's work-groups (first, one
+// per run of slots of a sequence) and the vocabulary pass's (row, part)
+// units, two per work-group (threads 0-255 and 256-511), in one launch.
+// They share nothing: the reorder reads the flags, positions, q/k/v, block
+// table and ctx_len and writes perm, q_phys and the window's cache rows;
+// the vocabulary pass reads the flags and logits and writes its partials.
+template <typename T, int SPW, bool VEC>
+__global__ __launch_bounds__(kReorderThreads) void step_front(ReorderArgs r, SelectArgs s, int nx) {
+    static_assert(kReorderThreads == 2 * kVocabThreads, "two vocabulary units per work-group");
+    const int blk = blockIdx.x;
+    const int nr = nx * r.B;
+    if (blk < nr) {
+        reorder_slots<T, SPW>(r, blk % nx, blk / nx);
+    } else {
+        __shared__ Stat s_red[2][4];
+        const int half = threadIdx.x / kVocabThreads;
+        const int unit = (blk - nr) * 2 + half;
+        vocab_unit<VEC>(s, unit, unit < s.B * s.W * s.nparts, threadIdx.x % kVocabThreads, s_red[half]);
+    }
+}
+
 // A Dual-Stream pass (thousands of slots) runs four slots per bf16
 // work-group; a decode window keeps one per slot.
 constexpr int kManySlots = 2048;
 
+static int reorder_spw(const ReorderArgs& a, int dtype) {
+    return dtype == WEDLM_BF16 && (int64_t)a.B * a.W >= kManySlots ? 4 : 1;
+}
+
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream) {
     dim3 block(kReorderThreads);
-    if (dtype == WEDLM_BF16 && (int64_t)a.B * a.W >= kManySlots) {
+    if (reorder_spw(a, dtype) == 4) {
         dim3 grid((a.W + 3) / 4, a.B);
         hipLaunchKernelGGL((reorder_rope_append<bf16_t, 4>), grid, block, 0, stream, a);
     } else if (dtype == WEDLM_F32) {
@@ -284,6 +313,24 @@ hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream) {
         hipLaunchKernelGGL((reorder_rope_append<bf16_t, 1>), dim3(a.W, a.B), block, 0, stream, a);
     }
     return hipGetLastError();
+}
+
+template <typename T, int SPW, bool VEC>
+static hipError_t launch_front_t(const ReorderArgs& r, const SelectArgs& s, hipStream_t st) {
+    const int nx = (r.W + SPW - 1) / SPW;
+    const long units = (long)s.B * s.W * s.nparts;
+    const long blocks = (long)nx * r.B + (units + 1) / 2;
+    hipLaunchKernelGGL((step_front<T, SPW, VEC>), dim3((unsigned)blocks), dim3(kReorderThreads), 0, st, r, s, nx);
+    return hipGetLastError();
+}
+
+hipError_t launch_step_front(const ReorderArgs& r, const SelectArgs& s, int dtype, hipStream_t st) {
+    const bool vec = vocab_vec(s);
+    if (reorder_spw(r, dtype) == 4)
+        return vec ? launch_front_t<bf16_t, 4, true>(r, s, st) : launch_front_t<bf16_t, 4, false>(r, s, st);
+    if (dtype == WEDLM_F32)
+        return vec ? launch_front_t<float, 1, true>(r, s, st) : launch_front_t<float, 1, false>(r, s, st);
+    return vec ? launch_front_t<bf16_t, 1, true>(r, s, st) : launch_front_t<bf16_t, 1, false>(r, s, st);
 }
 
 }  // namespace wedlm

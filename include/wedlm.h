@@ -14,6 +14,8 @@
  *                        distance-penalised fill rule (Eq. 11) and refill of
  *                        the window with new masks.
  *
+ * wedlm_decode_step runs the same three in one call with fewer launches.
+ *
  * The operations are defined on these pages (cited by title and section):
  *  - "WeDLM: Reconciling Diffusion Language Models with Standard Causal
  *    Attention for Fast Inference", paper-summary page (bud-325.pages.dev):
@@ -391,6 +393,71 @@ int wedlm_model_step(const wedlm_model *m, const wedlm_shape *s, const int32_t *
                      int32_t *argmax_out, float *entropy_out, int64_t *counters, void *hidden_out,
                      float alpha, float tau, double rope_base, int32_t max_ctx_len, void *workspace,
                      size_t ws_bytes, int32_t *dev_status, void *stream);
+
+/*
+ * wedlm_decode_step -- one whole streaming decode step: wedlm_reorder, then
+ * wedlm_step_attn, then wedlm_select_commit, with the results of those three
+ * calls in that order byte for byte, in three kernel launches instead of
+ * five.  (paper-summary page, "Method", inference paragraph and Eq. 11:
+ * the order of one step's work; "Key claims", sec. 5.2: the per-step
+ * forward is short enough that launch overhead matters, which the pages
+ * address with captured graphs.)
+ *
+ * The launches pair work that shares no memory: the reorder with the
+ * vocabulary statistics (both only read the window flags); the split-KV
+ * attention alone; the split combine with the commit / select / refill
+ * (the combine reads only the split partials and perm, the commit rewrites
+ * the window state and ctx_len).  On the small windows this removes two
+ * launch latencies from the step's critical path.
+ *
+ * Every pointer in *io means what the argument of the same name means in
+ * those three calls (shapes in s; V, max_ctx_len, mask_id, scale, alpha,
+ * tau, rope_base host values as there).  argmax_out, entropy_out, counters
+ * and dev_status may be NULL.
+ *   workspace / ws_bytes  device scratch of at least
+ *         wedlm_decode_step_workspace(s, max_ctx_len, V) bytes (the split
+ *         partials, then the vocabulary partials); contents need no
+ *         initialisation and are not preserved.
+ *   Errors: as the three calls (nothing is enqueued when a check fails).
+ */
+typedef struct {
+    /* window state, device, updated in place */
+    int32_t *tok;
+    uint8_t *filled;
+    int32_t *pos;
+    int32_t *ctx_len;
+    /* this step's inputs, device */
+    const void *q;          /* [B][W][Hq][D] logical slot order, before RoPE */
+    const void *k;          /* [B][W][Hkv][D] */
+    const void *v;          /* [B][W][Hkv][D] */
+    const float *logits;    /* [B][W][V] fp32 */
+    /* paged cache, device */
+    void *k_cache;
+    void *v_cache;
+    const int32_t *block_table;
+    /* outputs, device */
+    void *q_phys;           /* [B][W][Hq][D] */
+    int32_t *perm;          /* [B][W] */
+    void *out;              /* [B][W][Hq][D] logical slot order */
+    int32_t *n_commit;      /* [B] */
+    int32_t *committed;     /* [B][W] */
+    int32_t *argmax_out;    /* [B][W] or NULL */
+    float *entropy_out;     /* [B][W] or NULL */
+    int64_t *counters;      /* [B][2] accumulated, or NULL */
+    int32_t *dev_status;    /* or NULL */
+    /* host parameters */
+    int32_t V;
+    int32_t max_ctx_len;
+    int32_t mask_id;
+    float scale;            /* 0 means 1/sqrt(D) */
+    float alpha;
+    float tau;
+    double rope_base;
+} wedlm_step_io;
+
+size_t wedlm_decode_step_workspace(const wedlm_shape *s, int32_t max_ctx_len, int32_t V);
+int wedlm_decode_step(const wedlm_shape *s, const wedlm_step_io *io, void *workspace, size_t ws_bytes,
+                      void *stream);
 
 /*
  * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for

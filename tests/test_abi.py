@@ -104,6 +104,32 @@ def test_step_attn_validation():
     assert need >= 0
 
 
+def test_decode_step_validation_and_workspace():
+    from causal_attention_diffusion_amd.binding import WedlmStepIO
+    lib = wd.load_library()
+    s = _shape(max_pages=200)
+    fake = 0x1000   # never dereferenced: validation fails before any launch
+    io = WedlmStepIO(*([fake] * 16), None, None, None, None, 4096, 2000, 4096, 0.0, 0.25, 4.0, 1e6)
+    need = lib.wedlm_decode_step_workspace(C.byref(s), 2000, 4096)
+    # the split partials then the vocabulary partials, on 256-byte boundaries
+    attn = lib.wedlm_step_attn_workspace(C.byref(s), 2000)
+    assert need == (attn + 255) // 256 * 256 + lib.wedlm_select_commit_workspace(2, 16, 4096)
+    assert lib.wedlm_decode_step(C.byref(s), None, fake, need, None) == ERR_ARG
+    assert lib.wedlm_decode_step(C.byref(s), C.byref(io), fake, need - 1, None) == ERR_WS
+    assert lib.wedlm_decode_step(C.byref(s), C.byref(io), None, need, None) == ERR_WS
+    bad = WedlmStepIO(*([fake] * 16), None, None, None, None, 4096, 2000, 4096, 0.0, 0.25, 4.0, 0.5)
+    assert lib.wedlm_decode_step(C.byref(s), C.byref(bad), fake, need, None) == ERR_ARG     # rope_base
+    bad = WedlmStepIO(*([fake] * 16), None, None, None, None, 4096, 2000, 4096, 0.0, 0.25, float("inf"), 1e6)
+    assert lib.wedlm_decode_step(C.byref(s), C.byref(bad), fake, need, None) == ERR_ARG     # tau
+    bad = WedlmStepIO(*([fake] * 16), None, None, None, None, 4096, 5000, 4096, 0.0, 0.25, 4.0, 1e6)
+    assert lib.wedlm_decode_step(C.byref(s), C.byref(bad), fake, 1 << 30, None) == ERR_SHAPE  # beyond the table
+    nul = WedlmStepIO(*([fake] * 7), None, *([fake] * 8), None, None, None, None, 4096, 2000, 4096, 0.0, 0.25,
+                      4.0, 1e6)   # no logits
+    assert lib.wedlm_decode_step(C.byref(s), C.byref(nul), fake, need, None) == ERR_ARG
+    assert lib.wedlm_decode_step_workspace(C.byref(s), 2000, 0) == 0
+    assert lib.wedlm_decode_step(C.byref(_shape(W=65)), C.byref(io), fake, need, None) == ERR_SHAPE
+
+
 @pytest.mark.parametrize("B,W,Hq,Hkv,D,dt,L", [
     (4, 32, 32, 8, 128, 1, 32768), (32, 16, 32, 8, 128, 1, 8192), (1, 16, 32, 8, 128, 1, 2048),
     (1, 8, 4, 2, 64, 0, 64), (1, 64, 32, 8, 128, 1, 300), (3, 1, 8, 8, 64, 1, 0), (2, 16, 32, 4, 128, 1, 100000), (1, 64, 32, 8, 128, 1, 524224),

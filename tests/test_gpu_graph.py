@@ -1,6 +1,7 @@
 """Decode steps captured in a HIP graph replay exactly like the same steps
 run eagerly -- captured by torch and by the library's own capture API
-(wedlm_graph_*) -- and both match the oracle.
+(wedlm_graph_*) -- and both match the oracle; so do the same steps taken
+through the fused wedlm_decode_step.
 
 Three whole steps (reorder, attention, select/commit) on the Qwen3-8B-shaped
 single-layer workload are captured once and replayed four times, each replay
@@ -25,7 +26,7 @@ from parity_checks import rounding_exact
 pytestmark = pytest.mark.gpu
 
 
-def _decode_setup(dev, steps=3, V=4096):
+def _decode_setup(dev, steps=3, V=4096, fused=False):
     cfg = wl.CONFIGS["qwen3_l2048"]
     scfg = wl.SelectConfig("graph", B=cfg.B, W=cfg.W, V=V, seed=77, alpha=0.25, tau=6.0, steps=0,
                            kind="mixture")
@@ -41,9 +42,16 @@ def _decode_setup(dev, steps=3, V=4096):
     counters = torch.zeros((cfg.B, 2), dtype=torch.int64, device=dev)
     outs = torch.zeros((steps,) + tuple(t["out"].shape), dtype=t["out"].dtype, device=dev)
     state = (tok, t["filled"], t["pos"], t["ctx_len"], t["k_cache"], t["v_cache"])
+    ws_step = wd.decode_step_workspace_tensor(t["q"], t["k_cache"], t["block_table"], max_ctx, V)
 
     def run():
         for i in range(steps):
+            if fused:
+                wd.wedlm_decode_step(t["filled"], t["pos"], t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"],
+                                     t["v_cache"], t["block_table"], t["ctx_len"], t["perm"], outs[i],
+                                     cfg.rope_base, max_ctx, logits[i], tok, n_commit[i], committed[i],
+                                     scfg.alpha, scfg.tau, V, ws_step, counters=counters, dev_status=t["status"])
+                continue
             wd.wedlm_reorder(t["filled"], t["pos"], t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"],
                              t["v_cache"], t["block_table"], t["ctx_len"], t["perm"], cfg.rope_base,
                              dev_status=t["status"])
@@ -173,6 +181,29 @@ def test_native_capture_replays_like_eager(dev):
     with wd.capture(cap) as g:
         run()
     assert g.nodes() == (15, 0), g.nodes()
+    _replays_match(g.launch, restore, snapshot, ref, dev)
+    g.close()
+    assert t["status"].item() == 0
+
+
+def test_fused_steps_match_oracle_and_replay(dev):
+    # the same three steps through wedlm_decode_step: checked against the
+    # oracle's stream, then captured natively -- three launches per step (the
+    # reorder with the vocabulary statistics, split attention, the combine
+    # with the commit), 9 kernel nodes -- and replayed like the eager run
+    print("[graph] qwen3_l2048 x3 fused steps, V=4096, native capture", flush=True)
+    t, run, restore, snapshot, n_commit, check_oracle = _decode_setup(dev, fused=True)
+    run()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    assert int(n_commit.sum().item()) > 0
+    check_oracle(ref)
+    restore()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    with wd.capture(cap) as g:
+        run()
+    assert g.nodes() == (9, 0), g.nodes()
     _replays_match(g.launch, restore, snapshot, ref, dev)
     g.close()
     assert t["status"].item() == 0
