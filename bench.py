@@ -203,9 +203,7 @@ def summarise_decode(r):
 
 def summarise_select(r):
     return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
-            "eager_ms_per_step": r["eager_ms_per_step"], "step_call": r["step_call"],
-            **{k: r[k] for k in ("three_call_ms_per_step", "fused_ms_per_step") if k in r},
-            "window_tokens_per_s": r["value"],
+            "eager_ms_per_step": r["eager_ms_per_step"], "window_tokens_per_s": r["value"],
             "select_commit": r["select_commit"], "frac_of_hbm_peak": r["roofline"]["frac"], "P_c": r["P_c"]}
 
 
