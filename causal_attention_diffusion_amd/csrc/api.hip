@@ -729,10 +729,10 @@ extern "C" int wedlm_decode_step(const wedlm_shape* s, const wedlm_step_io* io, 
                           io->committed, io->argmax_out, io->entropy_out, io->counters, io->alpha, io->tau,
                           io->mask_id, ws + attn_bytes, ws_bytes - attn_bytes, &sa)))
         return rc;
-    // the front launch is one-dimensional with 512 work-items per work-group
-    // (one per slot, then two vocabulary units each): its work-item count
-    // must fit the dispatch's 32 bits
-    if ((int64_t)s->B * s->W + ((int64_t)s->B * s->W * sa.nparts + 1) / 2 >= (1ll << 23))
+    // the front launch is one-dimensional with 256 work-items per work-group
+    // (one per slot, then one per vocabulary unit): its work-item count must
+    // fit the dispatch's 32 bits
+    if ((int64_t)s->B * s->W + (int64_t)s->B * s->W * sa.nparts >= (1ll << 24))
         return fail(WEDLM_ERR_SHAPE, "wedlm_decode_step: grid too large (B=%d W=%d parts=%d)", s->B, s->W, sa.nparts);
     hipStream_t st = (hipStream_t)stream;
     if ((rc = hip_status(launch_step_front(ra, sa, s->dtype, st), "wedlm_decode_step front launch"))) return rc;

@@ -94,8 +94,9 @@ template <> struct Piece<bf16_t> {
 // decode window (a few dozen slots: every slot gets its own work-group and
 // CU), four for the thousands of slots of a Dual-Stream pass (a quarter of
 // the work-groups, each with four times the loads in flight).
-template <typename T, int SPW>
+template <typename T, int SPW, int NT>
 __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int b) {
+    static_assert(NT >= 4 * 64, "the angle table takes up to four slots x 64 threads");
     using P = Piece<T>;
     const int i0 = bx * SPW;           // first logical slot
     const int W = a.W, D = a.D, half = D / 2;
@@ -115,11 +116,11 @@ __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int 
     // kMaxItems items per thread is loaded before the permutation, the pages
     // and the angle tables are known.  (Plain code, no lambdas: arrays
     // captured by a lambda were kept in scratch memory by the compiler.)
-    constexpr int kMaxItems = SPW == 1 ? 2 : 6;
+    constexpr int kMaxItems = SPW == 1 ? 1024 / NT : 6;
     typename P::type r0[kMaxItems], r1[kMaxItems];
 #pragma unroll
     for (int u = 0; u < kMaxItems; ++u) {
-        const int it = tid + u * kReorderThreads;
+        const int it = tid + u * NT;
         if (it >= n_tot) continue;
         const int sl = it / n_all, jj = it - sl * n_all;
         const size_t row = row_first + sl;
@@ -213,11 +214,11 @@ __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int 
     __syncthreads();
 
     // Every later batch loads all its items before using any.
-    for (int base = tid; base < n_tot; base += kMaxItems * kReorderThreads) {
+    for (int base = tid; base < n_tot; base += kMaxItems * NT) {
         if (base != tid)   // the first batch is already loaded
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * kReorderThreads;
+            const int it = base + u * NT;
             if (it >= n_tot) continue;
             const int sl = it / n_all, jj = it - sl * n_all;
             const size_t row = row_first + sl;
@@ -236,7 +237,7 @@ __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int 
         }
 #pragma unroll
         for (int u = 0; u < kMaxItems; ++u) {
-            const int it = base + u * kReorderThreads;
+            const int it = base + u * NT;
             if (it >= n_tot) continue;
             const int sl = it / n_all, jj = it - sl * n_all;
             int r = rr[0];
@@ -270,27 +271,27 @@ __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int 
 
 template <typename T, int SPW>
 __global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderArgs a) {
-    reorder_slots<T, SPW>(a, blockIdx.x, blockIdx.y);
+    reorder_slots<T, SPW, kReorderThreads>(a, blockIdx.x, blockIdx.y);
 }
 
 // Front half of a fused decode step: the reorder's work-groups (first, one
-// per run of slots of a sequence) and the vocabulary pass's (row, part)
-// units, two per work-group (threads 0-255 and 256-511), in one launch.
-// They share nothing: the reorder reads the flags, positions, q/k/v, block
-// table and ctx_len and writes perm, q_phys and the window's cache rows;
-// the vocabulary pass reads the flags and logits and writes its partials.
+// per run of slots of a sequence, 256 threads each here) and the vocabulary
+// pass's (row, part) units, one per work-group as in vocab_stats, in one
+// launch.  They share nothing: the reorder reads the flags, positions,
+// q/k/v, block table and ctx_len and writes perm, q_phys and the window's
+// cache rows; the vocabulary pass reads the flags and logits and writes its
+// partials.  256-thread work-groups keep the vocabulary units at the
+// occupancy of their own launch (a 512-thread form, two units per
+// work-group, held fewer waves per CU and ran the units slower).
 template <typename T, int SPW, bool VEC>
-__global__ __launch_bounds__(kReorderThreads) void step_front(ReorderArgs r, SelectArgs s, int nx) {
-    static_assert(kReorderThreads == 2 * kVocabThreads, "two vocabulary units per work-group");
+__global__ __launch_bounds__(kVocabThreads) void step_front(ReorderArgs r, SelectArgs s, int nx) {
     const int blk = blockIdx.x;
     const int nr = nx * r.B;
     if (blk < nr) {
-        reorder_slots<T, SPW>(r, blk % nx, blk / nx);
+        reorder_slots<T, SPW, kVocabThreads>(r, blk % nx, blk / nx);
     } else {
-        __shared__ Stat s_red[2][4];
-        const int half = threadIdx.x / kVocabThreads;
-        const int unit = (blk - nr) * 2 + half;
-        vocab_unit<VEC>(s, unit, unit < s.B * s.W * s.nparts, threadIdx.x % kVocabThreads, s_red[half]);
+        __shared__ Stat s_red[4];
+        vocab_unit<VEC>(s, blk - nr, true, threadIdx.x, s_red);
     }
 }
 
@@ -319,8 +320,8 @@ template <typename T, int SPW, bool VEC>
 static hipError_t launch_front_t(const ReorderArgs& r, const SelectArgs& s, hipStream_t st) {
     const int nx = (r.W + SPW - 1) / SPW;
     const long units = (long)s.B * s.W * s.nparts;
-    const long blocks = (long)nx * r.B + (units + 1) / 2;
-    hipLaunchKernelGGL((step_front<T, SPW, VEC>), dim3((unsigned)blocks), dim3(kReorderThreads), 0, st, r, s, nx);
+    const long blocks = (long)nx * r.B + units;
+    hipLaunchKernelGGL((step_front<T, SPW, VEC>), dim3((unsigned)blocks), dim3(kVocabThreads), 0, st, r, s, nx);
     return hipGetLastError();
 }
 
