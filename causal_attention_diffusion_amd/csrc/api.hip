@@ -128,11 +128,17 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
         // One round of work-groups over the device (a bf16 work-group fills a
         // CU's LDS): the key work of every (sequence, KV head, row tile) at
         // the bound is cut so that the splits number about one per CU.  At
-        // least 256 keys per split so the per-split prologue and the fp32
-        // partial (RT*D*4 bytes) stay small next to the K/V a split streams.
+        // least 256 bf16 keys per split so the per-split prologue and the
+        // fp32 partial (RT*D*4 bytes) stay small next to the K/V a split
+        // streams; the fp32 kernel spends eight times the matrix-core
+        // instructions per key, so on small grids its splits go down to 64
+        // keys (one fp32 sequence, window 8, a few hundred keys: 16.3 vs
+        // 19.6 us per decode step; on a 2K-token bf16 prefix 128-key splits
+        // were slower than 256).
         const int64_t target = device_cus();
+        const int64_t min_keys = s->dtype == WEDLM_F32 ? 64 : 256;
         sk = (T * pairs + target - 1) / target;
-        if (sk < 256) sk = 256;
+        if (sk < min_keys) sk = min_keys;
     }
     sk = (sk + p.chunk - 1) / p.chunk * p.chunk;
     if (sk > (int64_t)kMaxSplitPages * kPage) sk = (int64_t)kMaxSplitPages * kPage;
