@@ -125,6 +125,51 @@ def test_fused_step_equals_three_calls(case, dev):
     print(f"[step] {case}: identical; commits per step {nc.sum(1).tolist()}", flush=True)
 
 
+@pytest.mark.parametrize("fault", ["bad_page", "bad_ctx"])
+def test_fused_step_reports_like_three_calls(fault, dev):
+    # a block-table entry outside the page pool (sequence 1) or a context
+    # length beyond the host bound (sequence 2): both forms raise the same
+    # device-status bit and still leave identical bytes everywhere
+    cfg = _cfg("ragged_b32", name=f"fault_{fault}", B=4, L_range=(300, 900), seed=97)
+    V, steps = 1024, 1
+    print(f"[step] {fault}", flush=True)
+    inp = wl.make_attn_inputs(cfg, spare_tokens=2 * cfg.W)
+    max_ctx = int(inp.ctx_len.max()) + cfg.W
+    scfg = wl.SelectConfig("fault", B=cfg.B, W=cfg.W, V=V, seed=3, alpha=0.25, tau=4.0, steps=0, kind="mixture")
+    logits = wl.make_logits_torch(scfg, 0, dev)
+    a = _Stream(inp, dev, V, steps, max_ctx)
+    f = _Stream(inp, dev, V, steps, max_ctx)
+    t, u = a.t, f.t
+    for x in (t, u):   # the fault goes into the device copies (the host draw built the cache)
+        if fault == "bad_page":
+            x["block_table"][1, 3] = 10 ** 6
+        else:
+            x["ctx_len"][2] = max_ctx + 1
+    ws_attn = wd.attn_workspace_tensor(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
+    ws_sel = wd.select_workspace_tensor(cfg.B, cfg.W, V, dev)
+    ws_step = wd.decode_step_workspace_tensor(u["q"], u["k_cache"], u["block_table"], max_ctx, V)
+    wd.wedlm_reorder(t["filled"], t["pos"], t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"], t["v_cache"],
+                     t["block_table"], t["ctx_len"], t["perm"], cfg.rope_base, dev_status=t["status"])
+    wd.wedlm_step_attn(t["q_phys"], t["k_cache"], t["v_cache"], t["block_table"], t["ctx_len"], t["perm"],
+                       a.outs[0], max_ctx_len=max_ctx, workspace=ws_attn, dev_status=t["status"])
+    a.keep(0)
+    wd.wedlm_select_commit(logits, a.tok, t["filled"], t["pos"], t["ctx_len"], a.n_commit[0], a.committed[0],
+                           scfg.alpha, scfg.tau, V, ws_sel, argmax_out=a.argmax[0], entropy_out=a.entropy[0],
+                           counters=a.counters)
+    wd.wedlm_decode_step(u["filled"], u["pos"], u["q"], u["k"], u["v"], u["q_phys"], u["k_cache"], u["v_cache"],
+                         u["block_table"], u["ctx_len"], u["perm"], f.outs[0], cfg.rope_base, max_ctx, logits,
+                         f.tok, f.n_commit[0], f.committed[0], scfg.alpha, scfg.tau, V, ws_step,
+                         argmax_out=f.argmax[0], entropy_out=f.entropy[0], counters=f.counters,
+                         dev_status=u["status"])
+    f.keep(0)
+    torch.cuda.synchronize()
+    want = 2 if fault == "bad_page" else 1   # WEDLM_DEV_BAD_PAGE / WEDLM_DEV_BAD_CTX
+    ra, rf = a.result(), f.result()
+    assert int(ra["status"].item()) & want, int(ra["status"].item())
+    for name in ra:
+        assert torch.equal(ra[name], rf[name]), f"{fault}: {name} differs"
+
+
 def test_fused_step_rejects_bad_arguments(dev):
     cfg = wl.CONFIGS["qwen3_l2048"]
     inp = wl.make_attn_inputs(cfg, spare_tokens=2 * cfg.W)
