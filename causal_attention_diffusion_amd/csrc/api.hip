@@ -74,6 +74,9 @@ static int reorder_args(const wedlm_shape* s, const uint8_t* filled, const int32
     a->B = s->B; a->W = s->W; a->Hq = s->Hq; a->Hkv = s->Hkv; a->D = s->D;
     a->max_pages = s->max_pages; a->num_pages = s->num_pages;
     a->log2_base = log2(rope_base);
+    a->part = nullptr;   // q, k, v from the given tensors
+    a->part_S = 0;
+    a->part_N = 0;
     return WEDLM_OK;
 }
 
@@ -321,7 +324,7 @@ extern "C" int wedlm_lmhead_select_commit(int32_t B, int32_t W, int32_t V, int32
 
 // ---------------------------------------------------------------- synthetic decoder step
 struct ModelLayout {
-    size_t x_res, h, q, k, v, qphys, perm, o, act, P, attn, lm, total;
+    size_t x_res, h, qphys, perm, o, act, P, attn, lm, total;
     size_t attn_bytes, lm_bytes;
     int Sqkv, So, Sgu, Sd;
 };
@@ -358,9 +361,6 @@ static int model_layout(const wedlm_model* m, const wedlm_shape* s, int32_t max_
     auto take = [&](size_t bytes) { const size_t r = o; o += up(bytes); return r; };
     L->x_res = take((size_t)M * d * 4);
     L->h = take((size_t)M * d * 2);
-    L->q = take((size_t)M * HqD * 2);
-    L->k = take((size_t)M * HkvD * 2);
-    L->v = take((size_t)M * HkvD * 2);
     L->qphys = take((size_t)M * HqD * 2);
     L->perm = take((size_t)M * 4);
     L->o = take((size_t)M * HqD * 2);
@@ -436,15 +436,21 @@ extern "C" int wedlm_model_step(const wedlm_model* m, const wedlm_shape* s, cons
         const void* next_norm = l + 1 < m->n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
         // q, k, v of the normalised window rows: one launch over [Wq; Wk; Wv]
         if ((rc = gemm(w.wq, w.wk, w.wv, HqD, HqD + HkvD, bf(L.h), Nqkv, d, L.Sqkv))) return rc;
+        // reorder + RoPE + append into this layer's cache straight from the
+        // projection's split partials (their bf16-rounded sums are the q, k,
+        // v a separate finish launch would store), then attention
         {
-            ModelRowArgs r = rows(bf(L.q), Nqkv, L.Sqkv, nullptr);
-            r.h1 = bf(L.k); r.h2 = bf(L.v); r.n1 = HqD; r.n2 = HqD + HkvD;
-            if ((rc = hip_status(launch_finish_split(r, st), "wedlm_model_step finish"))) return rc;
+            ReorderArgs ra;
+            const void* part = ws + L.P;   // q, k, v come from the partials (non-null for the checks)
+            if ((rc = reorder_args(s, filled, pos, part, part, part, ws + L.qphys, w.k_cache,
+                                   w.v_cache, block_table, ctx_len, reinterpret_cast<int32_t*>(ws + L.perm),
+                                   rope_base, dev_status, &ra)))
+                return rc;
+            ra.part = f32(L.P);
+            ra.part_S = L.Sqkv;
+            ra.part_N = Nqkv;
+            if ((rc = hip_status(launch_reorder_from_partials(ra, st), "wedlm_model_step reorder"))) return rc;
         }
-        // reorder + RoPE + append into this layer's cache, then attention
-        rc = wedlm_reorder(s, filled, pos, ws + L.q, ws + L.k, ws + L.v, ws + L.qphys, w.k_cache, w.v_cache,
-                           block_table, ctx_len, reinterpret_cast<int32_t*>(ws + L.perm), rope_base, dev_status, stream);
-        if (rc) return rc;
         rc = wedlm_step_attn(s, ws + L.qphys, w.k_cache, w.v_cache, block_table, ctx_len,
                              reinterpret_cast<int32_t*>(ws + L.perm), ws + L.o, 0.f, max_ctx_len, ws + L.attn,
                              L.attn_bytes, dev_status, stream);

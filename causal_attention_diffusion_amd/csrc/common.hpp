@@ -49,6 +49,22 @@ template <> struct DT<bf16_t> {
     __device__ static void store(bf16_t* p, size_t i, float x) { p[i].bits = f32_to_bf16(x); }
 };
 
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// four floats -> four bf16 (round to nearest even) as one 8-byte store
+__device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    return o;
+}
+__device__ __forceinline__ float4 unpack_bf16x4(uint2 u) {
+    return make_float4(bf16_to_f32(u.x & 0xffff), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffff),
+                       bf16_to_f32(u.y >> 16));
+}
+
 __device__ __forceinline__ void set_status(int32_t* st, uint32_t bit) {
     if (st) atomicOr(st, static_cast<int32_t>(bit));
 }

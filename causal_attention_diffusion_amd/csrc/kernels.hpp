@@ -23,6 +23,11 @@ struct ReorderArgs {
     int32_t* status;
     int B, W, Hq, Hkv, D, max_pages, num_pages;
     double log2_base;
+    // Projection form (reorder_from_partials): q, k and v are read as the
+    // bf16-rounded sums of part_S fp32 split-K partials [part_S][B*W][part_N]
+    // of the stacked [Wq; Wk; Wv] projection (q columns, then k, then v).
+    const float* part;
+    int part_S, part_N;
 };
 
 struct AttnArgs {
@@ -87,6 +92,8 @@ __device__ __forceinline__ int split_len(int T_len, int nsplit, int split_keys, 
 }
 
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
+// bf16 reorder whose q/k/v come from split-K partials (a.part)
+hipError_t launch_reorder_from_partials(const ReorderArgs& a, hipStream_t stream);
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
 // the split kernel alone (no combine)
 hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
@@ -97,10 +104,7 @@ struct ModelRowArgs {
     const bf16_t* embed;    // embed: [n_embed][N]
     int n_embed;
     float* x_res;           // residual stream [M][N] fp32
-    bf16_t* h;              // bf16 output [M][N] (split finish: columns [0, n1))
-    bf16_t* h1;             // split finish: columns [n1, n2) as [M][n2 - n1]
-    bf16_t* h2;             // split finish: columns [n2, N) as [M][N - n2]
-    int n1, n2;
+    bf16_t* h;              // bf16 output [M][N]
     const bf16_t* g;        // RMSNorm weight [N]
     const float* P;         // split-K partials [S][M][N] (SwiGLU: N = 2F, gate then up)
     int M, N, S;
@@ -127,7 +131,6 @@ int gemm_splits(int M, int N, int K);
 hipError_t launch_gemm(GemmArgs a, hipStream_t stream);
 hipError_t launch_embed_rmsnorm(const ModelRowArgs& a, hipStream_t stream);
 hipError_t launch_add_rmsnorm(const ModelRowArgs& a, hipStream_t stream);
-hipError_t launch_finish_split(const ModelRowArgs& a, hipStream_t stream);
 hipError_t launch_finish_swiglu(const ModelRowArgs& a, hipStream_t stream);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t stream);
 hipError_t launch_dual_layout(uint8_t* filled_m, int32_t* pos_m, int32_t* ctx_m, int32_t* bt_m, int32_t* pos_p,

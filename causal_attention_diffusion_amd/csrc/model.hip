@@ -38,21 +38,6 @@ using GemmWide = TileCfg<256, 128, 64, 3, 4>;
 
 __device__ __forceinline__ float silu(float g) { return g / (1.f + __expf(-g)); }
 
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-// four floats -> four bf16 (round to nearest even) as one 8-byte store
-__device__ __forceinline__ uint2 pack_bf16x4(float4 v) {
-    uint2 o;
-    o.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    o.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
-    return o;
-}
-__device__ __forceinline__ float4 unpack_bf16x4(uint2 u) {
-    return make_float4(bf16_to_f32(u.x & 0xffff), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xffff),
-                       bf16_to_f32(u.y >> 16));
-}
 
 // Row kernels run one work-group of kRowThreads threads per row: a thread
 // owns the float4 columns tid, tid + kRowThreads, ... (one each at a
@@ -131,22 +116,6 @@ __device__ __forceinline__ float4 sum_splits(const ModelRowArgs& a, size_t i4) {
     float4 v = P[i4];
     for (int s = 1; s < a.S; ++s) v = add4(v, P[s * plane4 + i4]);
     return v;
-}
-
-// Stacked projection outputs: bf16(sum_s P[s][m][n]) to h (n < n1), h1
-// (n1 <= n < n2) or h2 (n >= n2), each row-major with its own width.
-__global__ __launch_bounds__(256) void finish_split(ModelRowArgs a) {
-    const int N4 = a.N / 4;
-    const size_t total4 = (size_t)a.M * N4;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (size_t)gridDim.x * 256) {
-        const int m = (int)(i / N4);
-        const int n = (int)(i - (size_t)m * N4) * 4;
-        const uint2 o = pack_bf16x4(sum_splits(a, i));
-        bf16_t* dst = n < a.n1 ? a.h + (size_t)m * a.n1 + n
-                               : (n < a.n2 ? a.h1 + (size_t)m * (a.n2 - a.n1) + (n - a.n1)
-                                           : a.h2 + (size_t)m * (a.N - a.n2) + (n - a.n2));
-        *reinterpret_cast<uint2*>(dst) = o;
-    }
 }
 
 // SwiGLU activation from the stacked gate / up projection (N = 2F columns,
@@ -351,10 +320,6 @@ hipError_t launch_add_rmsnorm(const ModelRowArgs& a, hipStream_t st) {
 static unsigned row_blocks(size_t items) {
     const size_t b = (items + 255) / 256;
     return (unsigned)(b < 4096 ? b : 4096);
-}
-hipError_t launch_finish_split(const ModelRowArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL(finish_split, dim3(row_blocks((size_t)a.M * a.N / 4)), dim3(256), 0, st, a);
-    return hipGetLastError();
 }
 hipError_t launch_finish_swiglu(const ModelRowArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(finish_swiglu, dim3(row_blocks((size_t)a.M * a.N / 8)), dim3(256), 0, st, a);

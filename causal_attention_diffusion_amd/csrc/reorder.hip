@@ -94,8 +94,30 @@ template <> struct Piece<bf16_t> {
 // decode window (a few dozen slots: every slot gets its own work-group and
 // CU), four for the thousands of slots of a Dual-Stream pass (a quarter of
 // the work-groups, each with four times the loads in flight).
-template <typename T, int SPW, int NT>
+// Projection form: four consecutive columns n .. n+3 of row m of the stacked
+// q/k/v projection, summed over the split-K partials in split order and
+// rounded to bf16, exactly as the projection's own finish would store them.
+// The partials are loaded four splits at a time (all four in flight) and
+// added in split order.
+__device__ __forceinline__ uint2 part_bf16x4(const ReorderArgs& a, size_t m, int n) {
+    const float* p = a.part + m * a.part_N + n;
+    const size_t plane = (size_t)a.B * a.W * a.part_N;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < a.part_S; s0 += 4) {
+        float4 w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (s0 + j < a.part_S) w[j] = *reinterpret_cast<const float4*>(p + (size_t)(s0 + j) * plane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (s0 + j < a.part_S) v = s0 + j == 0 ? w[0] : add4(v, w[j]);
+    }
+    return pack_bf16x4(v);
+}
+
+template <typename T, int SPW, int NT, bool FROM_PART = false>
 __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int b) {
+    static_assert(!FROM_PART || sizeof(T) == 2, "the projection form is bf16");
     static_assert(NT >= 4 * 64, "the angle table takes up to four slots x 64 threads");
     using P = Piece<T>;
     const int i0 = bx * SPW;           // first logical slot
@@ -128,13 +150,22 @@ __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int 
             const bool isq = jj < qn;
             const int j = isq ? jj : jj - qn;
             const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-            const T* src = isq ? static_cast<const T*>(a.q) + (row * a.Hq + hh) * D + c
-                               : static_cast<const T*>(a.k) + (row * a.Hkv + hh) * D + c;
-            r0[u] = P::load(src);
-            r1[u] = P::load(src + half);
+            if constexpr (FROM_PART) {
+                const int n = (isq ? 0 : a.Hq * D) + hh * D + c;
+                r0[u] = part_bf16x4(a, row, n);
+                r1[u] = part_bf16x4(a, row, n + half);
+            } else {
+                const T* src = isq ? static_cast<const T*>(a.q) + (row * a.Hq + hh) * D + c
+                                   : static_cast<const T*>(a.k) + (row * a.Hkv + hh) * D + c;
+                r0[u] = P::load(src);
+                r1[u] = P::load(src + half);
+            }
         } else {
             const int j = jj - qn - kn;
-            r0[u] = P::load(static_cast<const T*>(a.v) + row * a.Hkv * D + (size_t)j * 4);
+            if constexpr (FROM_PART)
+                r0[u] = part_bf16x4(a, row, (a.Hq + a.Hkv) * D + j * 4);
+            else
+                r0[u] = P::load(static_cast<const T*>(a.v) + row * a.Hkv * D + (size_t)j * 4);
         }
     }
 
@@ -226,13 +257,22 @@ __device__ __forceinline__ void reorder_slots(const ReorderArgs& a, int bx, int 
                 const bool isq = jj < qn;
                 const int j = isq ? jj : jj - qn;
                 const int hh = j / (half / 4), c = (j % (half / 4)) * 4;
-                const T* src = isq ? static_cast<const T*>(a.q) + (row * a.Hq + hh) * D + c
-                                   : static_cast<const T*>(a.k) + (row * a.Hkv + hh) * D + c;
-                r0[u] = P::load(src);
-                r1[u] = P::load(src + half);
+                if constexpr (FROM_PART) {
+                    const int n = (isq ? 0 : a.Hq * D) + hh * D + c;
+                    r0[u] = part_bf16x4(a, row, n);
+                    r1[u] = part_bf16x4(a, row, n + half);
+                } else {
+                    const T* src = isq ? static_cast<const T*>(a.q) + (row * a.Hq + hh) * D + c
+                                       : static_cast<const T*>(a.k) + (row * a.Hkv + hh) * D + c;
+                    r0[u] = P::load(src);
+                    r1[u] = P::load(src + half);
+                }
             } else {
                 const int j = jj - qn - kn;
-                r0[u] = P::load(static_cast<const T*>(a.v) + row * a.Hkv * D + (size_t)j * 4);
+                if constexpr (FROM_PART)
+                    r0[u] = part_bf16x4(a, row, (a.Hq + a.Hkv) * D + j * 4);
+                else
+                    r0[u] = P::load(static_cast<const T*>(a.v) + row * a.Hkv * D + (size_t)j * 4);
             }
         }
 #pragma unroll
@@ -274,6 +314,13 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_rope_append(ReorderAr
     reorder_slots<T, SPW, kReorderThreads>(a, blockIdx.x, blockIdx.y);
 }
 
+// The decoder step's reorder straight from its [Wq; Wk; Wv] projection's
+// split-K partials: the same slots, rotations and stores, with no separate
+// launch to sum the partials into bf16 q, k and v first.
+__global__ __launch_bounds__(kReorderThreads) void reorder_from_partials(ReorderArgs a) {
+    reorder_slots<bf16_t, 1, kReorderThreads, true>(a, blockIdx.x, blockIdx.y);
+}
+
 // Front half of a fused decode step: the reorder's work-groups (first, one
 // per run of slots of a sequence, 256 threads each here) and the vocabulary
 // pass's (row, part) units, one per work-group as in vocab_stats, in one
@@ -313,6 +360,11 @@ hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream) {
     } else {
         hipLaunchKernelGGL((reorder_rope_append<bf16_t, 1>), dim3(a.W, a.B), block, 0, stream, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_reorder_from_partials(const ReorderArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(reorder_from_partials, dim3(a.W, a.B), dim3(kReorderThreads), 0, stream, a);
     return hipGetLastError();
 }
 
