@@ -1,6 +1,7 @@
 // attn.hip -- fp32 windowed causal grouped-query attention of one WeDLM
-// decode step over a paged prefix KV cache (gfx950, MFMA), and the split-KV
-// combine shared by the fp32 and bf16 kernels.
+// decode step over a paged prefix KV cache (gfx950, MFMA), the split-KV
+// combine shared by the fp32 and bf16 kernels, and the fused decode step's
+// back launch (the combine beside the commit / select / refill).
 //
 // Pages: "WeDLM: Reconciling Diffusion Language Models with Standard Causal
 // Attention for Fast Inference", paper-summary page, "Key claims" (paper

@@ -18,6 +18,9 @@
 // cache at token ctx_len[b] + r.
 // The work is tiny (B*W*(Hq+2Hkv)*D elements) and latency-bound; angles and
 // rotations are float64 so that positions up to 2^31 keep full accuracy.
+// The same body also runs inside the fused decode step's front launch
+// (beside the vocabulary pass) and, for the synthetic decoder, straight from
+// the q/k/v projection's split partials.
 #include "select.hpp"
 
 namespace wedlm {
