@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--vocab", type=int, default=151936)
     ap.add_argument("--logit-ring", type=int, default=4, help="distinct logits buffers cycled over steps")
     ap.add_argument("--split-keys", type=int, default=0, help="override keys per split-KV work-group")
+    ap.add_argument("--attn-tail", type=int, default=-1,
+                    help="tail splits: sequences cut in two (-1 automatic, 0 off)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true",
                     help="long_b4 only: skip the summaries of the other decode-step workloads and of the "
@@ -224,6 +226,7 @@ def decode_leg(args, workload, with_cpu):
     inp = wl.make_attn_inputs(cfg, spare_tokens=spare)
     t = wl.device_attn_inputs(inp, dev)
     wd.wedlm_set_attn_split_keys(args.split_keys)
+    wd.wedlm_set_attn_tail(args.attn_tail)
 
     B, W = cfg.B, cfg.W
     mask_id = args.vocab
@@ -240,6 +243,7 @@ def decode_leg(args, workload, with_cpu):
     committed = torch.empty((B, W), dtype=torch.int32, device=dev)
     argmax_hist = torch.empty((total_steps, B, W), dtype=torch.int32, device=dev)  # -1 on unmasked slots
     nsplit, split_keys = wd.wedlm_attn_plan(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
+    tail = wd.wedlm_attn_tail(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
 
     def reorder():
         wd.wedlm_reorder(filled, pos, t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"], t["v_cache"],
@@ -436,7 +440,7 @@ def decode_leg(args, workload, with_cpu):
                                f"prefix={int(inp.ctx_len.max()) if cfg.L_range is None else str(cfg.L_range)} "
                                f"page=16 vocab={args.vocab} streaming decode step (reorder+attn+select/commit)",
                    "batch": B, "window": W, "prefix_tokens_at_start": int(ctx_start.max()),
-                   "vocab": args.vocab, "split_kv": [nsplit, split_keys]},
+                   "vocab": args.vocab, "split_kv": [nsplit, split_keys], "tail_splits": tail},
         "steps_per_s": round(1e3 / ms_step, 2),
         "attn": {"avg_ms": round(attn_avg_ms, 5), "alg_bytes_per_launch": int(mean_attn_bytes),
                  "GB_per_s": round(achieved, 1), "prefix_tokens": [int(x) for x in L_now],

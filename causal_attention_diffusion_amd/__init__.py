@@ -44,6 +44,9 @@ from .binding import (  # noqa: F401
     wedlm_select_commit,
     wedlm_select_commit_workspace,
     wedlm_set_attn_split_keys,
+    wedlm_attn_tail,
+    attn_tail,
+    wedlm_set_attn_tail,
     wedlm_set_select_parts,
     wedlm_step_attn,
     wedlm_step_attn_noalloc,

@@ -104,6 +104,10 @@ def load_library():
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
     lib.wedlm_set_attn_split_keys.restype = C.c_int
+    lib.wedlm_attn_tail.argtypes = [S, i32]
+    lib.wedlm_attn_tail.restype = i32
+    lib.wedlm_set_attn_tail.argtypes = [i32]
+    lib.wedlm_set_attn_tail.restype = C.c_int
     lib.wedlm_set_select_parts.argtypes = [i32]
     lib.wedlm_set_select_parts.restype = C.c_int
     lib.wedlm_graph_begin.argtypes = [P]
@@ -274,6 +278,24 @@ def attn_plan(B, W, Hq, Hkv, D, max_pages, num_pages, dtype, max_ctx_len):
 
 def wedlm_set_attn_split_keys(keys: int):
     _check(load_library().wedlm_set_attn_split_keys(int(keys)))
+
+
+def wedlm_attn_tail(q_phys, k_cache, block_table, max_ctx_len: int) -> int:
+    """Sequences the attention plan cuts in two (tail splits), 0 if none."""
+    s = _shape_from(q_phys, k_cache, block_table)
+    n = int(load_library().wedlm_attn_tail(C.byref(s), int(max_ctx_len)))
+    if n < 0:
+        raise WedlmError("wedlm_attn_tail: bad shape or bound")
+    return n
+
+
+def attn_tail(B, W, Hq, Hkv, D, max_pages, num_pages, dtype, max_ctx_len) -> int:
+    s = make_shape(B, W, Hq, Hkv, D, max_pages, num_pages, dtype)
+    return int(load_library().wedlm_attn_tail(C.byref(s), int(max_ctx_len)))
+
+
+def wedlm_set_attn_tail(n: int):
+    _check(load_library().wedlm_set_attn_tail(int(n)))
 
 
 def wedlm_set_select_parts(parts: int):

@@ -93,6 +93,7 @@ extern "C" int wedlm_reorder(const wedlm_shape* s, const uint8_t* filled, const 
 
 // ---------------------------------------------------------------- attention plan
 static std::atomic<int32_t> g_split_override{0};   // process-wide, read by every plan
+static std::atomic<int32_t> g_tail_override{-1};   // tail splits: -1 automatic, 0 off, n > 0 that many
 
 // Compute units of the current device (cached per device; 256 on MI355X).
 static int device_cus() {
@@ -109,12 +110,13 @@ static int device_cus() {
 static const int64_t kMaxContext = 524288;  // keys incl. the window (at most 64 splits)
 
 struct Plan {
-    int nw, chunk, RT, row_tiles, nsplit, split_keys;
-    size_t ws_bytes, off_ml;
+    int nw, chunk, RT, row_tiles, nsplit, split_keys, tail, cus;
+    size_t ws_bytes, off_ml, off_tail;
 };
 
 static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     Plan p;
+    p.cus = (int)device_cus();
     const int G = s->Hq / s->Hkv;
     const int M = s->W * G;
     p.nw = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
@@ -152,6 +154,26 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     p.split_keys = (int)sk;
     p.nsplit = (int)((T + sk - 1) / sk);
     if (p.nsplit < 1) p.nsplit = 1;
+    // Tail splits: a one-split bf16 plan whose (sequence, KV head) groups
+    // fill at least half of the CUs in one round is bound by its longest
+    // sequences, each streaming alone on one CU after the short ones are
+    // done.  The longest quarter of the sequences (ranked on the device from
+    // ctx_len) get a second work-group for the back half of their keys;
+    // those are dispatched after the first round and start on the CUs the
+    // shortest sequences free.  3/8 of the batch measured best at the
+    // ragged 32-sequence shape (a quarter, a half, three quarters within
+    // 1-2 % below it).
+    p.tail = 0;
+    {
+        const int32_t ov = g_tail_override.load(std::memory_order_relaxed);
+        const int64_t cus = device_cus();
+        const bool fits = s->dtype == WEDLM_BF16 && p.nsplit == 1 && p.row_tiles == 1 && s->B >= 2 &&
+                          s->B <= kMaxSplitPages / 2 && pairs <= cus;
+        if (fits && ov > 0) p.tail = ov < s->B ? ov : s->B;
+        else if (fits && ov < 0 && 2 * pairs >= cus && s->B >= 4) p.tail = (3 * s->B + 7) / 8;
+        if (p.tail > 0) p.nsplit = 2;
+    }
+    p.off_tail = 0;
     if (p.nsplit == 1) {
         p.ws_bytes = 0;
         p.off_ml = 0;
@@ -160,6 +182,10 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
         const size_t o_bytes = (rows * s->D * sizeof(float) + 255) / 256 * 256;
         p.off_ml = o_bytes;
         p.ws_bytes = o_bytes + (rows * sizeof(float2) + 255) / 256 * 256;
+        if (p.tail > 0) {
+            p.off_tail = p.ws_bytes;
+            p.ws_bytes += ((size_t)p.tail * s->Hkv * sizeof(int32_t) + 255) / 256 * 256;
+        }
     }
     return p;
 }
@@ -505,6 +531,19 @@ extern "C" int wedlm_set_attn_split_keys(int32_t keys) {
     return WEDLM_OK;
 }
 
+extern "C" int32_t wedlm_attn_tail(const wedlm_shape* s, int32_t max_ctx_len) {
+    if (check_shape(s) || max_ctx_len < 0 || (int64_t)max_ctx_len + s->W > kMaxContext) return -1;
+    g_err[0] = 0;
+    return make_plan(s, max_ctx_len).tail;
+}
+
+extern "C" int wedlm_set_attn_tail(int32_t n) {
+    if (n < -1) return fail(WEDLM_ERR_ARG, "tail must be -1 (automatic), 0 (off) or a sequence count");
+    g_tail_override.store(n, std::memory_order_relaxed);
+    g_err[0] = 0;
+    return WEDLM_OK;
+}
+
 extern "C" size_t wedlm_step_attn_workspace(const wedlm_shape* s, int32_t max_ctx_len) {
     if (check_shape(s) || max_ctx_len < 0) return 0;
     return make_plan(s, max_ctx_len).ws_bytes;
@@ -599,6 +638,9 @@ static int attn_args(const wedlm_shape* s, const void* q_phys, const void* k_cac
     a.ctx_len = ctx_len; a.perm = perm; a.out = out;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = p.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + p.off_ml) : nullptr;
+    a.tail = p.tail;
+    a.tail_free = p.tail ? (int)(p.cus > (int64_t)s->B * s->Hkv ? p.cus - (int64_t)s->B * s->Hkv : 0) : 0;
+    a.tail_seq = p.tail ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.off_tail) : nullptr;
     a.status = dev_status;
     a.B = s->B; a.W = s->W; a.Hq = s->Hq; a.Hkv = s->Hkv; a.G = s->Hq / s->Hkv; a.M = s->W * a.G;
     a.max_pages = s->max_pages; a.num_pages = s->num_pages;

@@ -292,14 +292,27 @@ __device__ __forceinline__ void combine_rows(const AttnArgs& a, int blk, int tid
     const int lr = tid / D4;
     const int d = (tid % D4) * 4;
     const long row = (long)blk * RPB + lr;
-    const int npid = a.B * a.Hkv * a.row_tiles;
-    const int pid = (int)(row / a.RT);
-    if (pid >= npid) return;
-    const int m_loc = (int)(row - (long)pid * a.RT);
-    const int rt = pid % a.row_tiles;
-    const int bk = pid / a.row_tiles;
-    const int kvh = bk % a.Hkv;
-    const int b = bk / a.Hkv;
+    int pid, m_loc, rt, kvh, b;
+    if (a.tail > 0) {
+        // tail plan: only the sequences cut in two have partials to merge;
+        // group g is the second half's work-group, which named its sequence
+        const int g = (int)(row / a.RT);
+        if (g >= a.tail * a.Hkv) return;
+        m_loc = (int)(row - (long)g * a.RT);
+        kvh = g % a.Hkv;
+        b = a.tail_seq[g];
+        rt = 0;
+        pid = b * a.Hkv + kvh;
+    } else {
+        const int npid = a.B * a.Hkv * a.row_tiles;
+        pid = (int)(row / a.RT);
+        if (pid >= npid) return;
+        m_loc = (int)(row - (long)pid * a.RT);
+        rt = pid % a.row_tiles;
+        const int bk = pid / a.row_tiles;
+        kvh = bk % a.Hkv;
+        b = bk / a.Hkv;
+    }
     const int m = rt * a.RT + m_loc;
     if (m >= a.M) return;
     const size_t base = (size_t)pid * a.nsplit * a.RT + m_loc;
@@ -386,7 +399,7 @@ __global__ __launch_bounds__(256) void step_back(AttnArgs a, SelectArgs s, int n
 template <int D>
 static unsigned combine_blocks(const AttnArgs& a) {
     constexpr int RPB = 256 / (D / 4);
-    const long rows = (long)a.B * a.Hkv * a.row_tiles * a.RT;
+    const long rows = a.tail > 0 ? (long)a.tail * a.Hkv * a.RT : (long)a.B * a.Hkv * a.row_tiles * a.RT;
     return (unsigned)((rows + RPB - 1) / RPB);
 }
 template <typename T, int D>

@@ -235,7 +235,58 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
     // and the short ones fill the tail.
     const int nbk = a.B * a.Hkv;
     int split, bk, rt;
-    if (a.row_tiles == 1) {
+    bool cut = false;   // tail plan: this (sequence, KV head) is cut in two ...
+    int tail_h = 0;     // ... at this key
+    if (a.tail > 0) {
+        // tail plan: rank the sequences by visible keys (longest first, ties
+        // by index) from ctx_len, staged in the block-table slice's LDS
+        __shared__ int s_tail_b, s_tail_cut, s_tail_rank;
+        int* s_T = s_pages;              // [B] keys of each sequence
+        int* s_byrank = s_pages + a.B;   // [B] keys of the sequence of each rank
+        const int gid = (int)blockIdx.x;
+        const bool second = gid >= nbk;
+        const int e = second ? (gid - nbk) / a.Hkv : 0;
+        const int my_b = second ? -1 : (nbk - 1 - gid) / a.Hkv;
+        for (int i = tid; i < a.B; i += C::NT) {
+            const int Li = a.ctx_len[i];
+            const bool ok = Li >= 0 && Li <= a.max_ctx && (int64_t)Li + a.W <= (int64_t)a.max_pages * kPage;
+            s_T[i] = ok ? Li + a.W : 0;
+        }
+        __syncthreads();
+        for (int i = tid; i < a.B; i += C::NT) {
+            const int Ti = s_T[i];
+            int rank = 0;
+            for (int j = 0; j < a.B; ++j) {
+                const int Tj = s_T[j];
+                rank += (Tj > Ti) | ((Tj == Ti) & (j < i));
+            }
+            s_byrank[rank] = Ti;
+            if (i == my_b) {
+                s_tail_cut = rank < a.tail;
+                s_tail_rank = rank;
+            }
+            if (second && rank == e) s_tail_b = i;
+        }
+        __syncthreads();
+        const int tb = second ? s_tail_b : my_b;
+        const int kv = second ? (gid - nbk) % a.Hkv : (nbk - 1 - gid) % a.Hkv;
+        split = second ? 1 : 0;
+        cut = second || s_tail_cut;
+        bk = tb * a.Hkv + kv;
+        if (cut) {
+            // back half j = rank * Hkv + head starts at once (j < tail_free)
+            // or after the first round of the (j - tail_free) / Hkv-th
+            // shortest sequence
+            const int j = (second ? e : s_tail_rank) * a.Hkv + kv;
+            const int start = j < a.tail_free ? 0 : s_byrank[a.B - 1 - min((j - a.tail_free) / a.Hkv, a.B - 1)];
+            const int Tb = s_T[tb];
+            tail_h = tail_cut(Tb, start, a.split_align);
+        }
+        rt = 0;
+        if (second && tid == 0) a.tail_seq[gid - nbk] = tb;
+        __syncthreads();   // s_T (s_pages) read by all before the block-table slice lands there
+        bk = nbk - 1 - bk;  // undone by the common reversal below
+    } else if (a.row_tiles == 1) {
         split = blockIdx.x / nbk;
         bk = blockIdx.x - split * nbk;
         rt = 0;
@@ -259,10 +310,19 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         L = 0;
     }
     const int T_len = ctx_ok ? L + a.W : 0;
-    const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
-    const int k_begin = split * sk;
-    const int k_end = min(T_len, k_begin + sk);
-    if (k_begin >= k_end && a.nsplit > 1) {
+    int k_begin, k_end;
+    if (a.tail > 0) {
+        const int h = cut ? min(tail_h, T_len) : T_len;
+        k_begin = split == 0 ? 0 : h;
+        k_end = split == 0 ? h : T_len;
+    } else {
+        const int sk = split_len(T_len, a.nsplit, a.split_keys, a.split_align);
+        k_begin = split * sk;
+        k_end = min(T_len, k_begin + sk);
+    }
+    // one split covers the sequence: the rows are written out directly
+    const bool direct = a.nsplit == 1 || (a.tail > 0 && !cut);
+    if (k_begin >= k_end && !direct) {
         // no key here: the split's rows get an empty partial (m = -inf, l = 0),
         // which attn_combine weighs zero without reading its O
         const size_t prow0 = ((size_t)pid * a.nsplit + split) * RT;
@@ -645,7 +705,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
                 o.x += wgt * v.x; o.y += wgt * v.y; o.z += wgt * v.z; o.w += wgt * v.w;
             }
         }
-        if (a.nsplit == 1) {
+        if (direct) {
             const int rr = mm / a.G;
             const int hh = kvh * a.G + mm % a.G;
             const int slot = a.perm[(size_t)b * a.W + rr];
@@ -671,6 +731,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
 // split); with several row tiles the (sequence, KV head, split) groups are
 // padded to a multiple of 8 (see the id mapping in the kernel).
 static unsigned bf16_split_grid(const AttnArgs& a) {
+    if (a.tail > 0) return (unsigned)((long)a.B * a.Hkv + (long)a.tail * a.Hkv);
     const long groups = (long)a.B * a.Hkv * a.nsplit;
     if (a.row_tiles == 1) return (unsigned)groups;
     return (unsigned)((groups + 7) / 8 * 8 * a.row_tiles);

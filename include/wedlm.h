@@ -475,6 +475,30 @@ int wedlm_attn_plan(const wedlm_shape *s, int32_t max_ctx_len, int32_t *nsplit,
 int wedlm_set_attn_split_keys(int32_t keys);
 
 /*
+ * Tail splits (bf16).  When the plan has one split per (sequence, KV head)
+ * and those work-groups fill between half and all of the CUs in one round,
+ * the call is bound by its longest sequences, each streaming alone on one
+ * CU once the short ones are done.  The plan then cuts the `tail` longest
+ * sequences of the batch in two (ranked on the device from ctx_len at each
+ * call, longest first, ties by index): one more work-group per KV head
+ * takes the back part of each, and only their rows go through split
+ * partials and the combine.  The cut is placed so both parts would end
+ * together if every work-group streamed at one rate and the back part
+ * started when a CU frees up (rounded up to 64 keys).  The result
+ * is the same softmax attention; wedlm_attn_plan then reports nsplit = 2.
+ *
+ * wedlm_attn_tail -- the number of sequences the plan cuts for this shape
+ * and bound (0: tail splits off), or -1 on a bad shape.
+ * wedlm_set_attn_tail -- process-wide override: -1 automatic (3/8 of the
+ * batch, rounded up, where the plan qualifies), 0 off, n > 0 the n longest
+ * (at most B) wherever the plan has one split per group, one row tile, no
+ * more groups than CUs and B <= 1024.  Affects later workspace queries and
+ * calls alike.
+ */
+int32_t wedlm_attn_tail(const wedlm_shape *s, int32_t max_ctx_len);
+int wedlm_set_attn_tail(int32_t n);
+
+/*
  * Graph capture of decode steps -- the launch-latency remedy the pages
  * point to for a small causal prefill over the window ("Key claims",
  * sec. 5.2: the step stays a standard causal forward, so graph capture

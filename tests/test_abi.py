@@ -137,12 +137,43 @@ def test_decode_step_validation_and_workspace():
 def test_attention_plan_covers_every_key(B, W, Hq, Hkv, D, dt, L):
     mp = (L + W + 15) // 16
     ns, sk = wd.attn_plan(B, W, Hq, Hkv, D, mp, B * mp, dt, L)
+    tail = wd.attn_tail(B, W, Hq, Hkv, D, mp, B * mp, dt, L)
     assert ns >= 1 and sk >= 32 and sk % 32 == 0 and sk <= 32768
-    assert ns * sk >= L + W                 # the grid covers every visible key
-    assert (ns - 1) * sk < L + W            # and no split is wholly past the end
+    if tail:
+        # tail splits: the first work-group of a sequence covers it all (or
+        # its front half), the second the back half of a cut sequence
+        assert ns == 2 and sk >= L + W and 0 < tail <= B
+    else:
+        assert ns * sk >= L + W                 # the grid covers every visible key
+        assert (ns - 1) * sk < L + W            # and no split is wholly past the end
     s = _shape(B=B, W=W, Hq=Hq, Hkv=Hkv, D=D, max_pages=mp, num_pages=B * mp, dtype=dt)
     ws = wd.load_library().wedlm_step_attn_workspace(C.byref(s), L)
     assert (ws == 0) == (ns == 1)
+
+
+def test_tail_split_plan():
+    # one split per (sequence, KV head) filling 128..256 CUs in one round:
+    # the longest 3/8 of the batch are cut in two (bf16 only)
+    assert wd.attn_tail(32, 16, 32, 8, 128, 513, 32 * 513, 1, 8192) == 12
+    assert wd.attn_plan(32, 16, 32, 8, 128, 513, 32 * 513, 1, 8192)[0] == 2
+    assert wd.attn_tail(32, 16, 32, 8, 128, 513, 32 * 513, 0, 8192) == 0       # fp32
+    assert wd.attn_tail(8, 16, 32, 8, 128, 513, 8 * 513, 1, 8192) == 0         # 64 groups: under half the CUs
+    assert wd.attn_tail(64, 16, 32, 8, 128, 513, 64 * 513, 1, 8192) == 0       # 512 groups: two rounds
+    assert wd.attn_tail(4, 32, 32, 8, 128, 2100, 4 * 2100, 1, 32768) == 0      # several splits already
+    assert wd.attn_tail(2, 64, 32, 8, 128, 200, 400, 1, 3000) == 0             # two row tiles
+    try:
+        wd.wedlm_set_attn_tail(0)
+        assert wd.attn_tail(32, 16, 32, 8, 128, 513, 32 * 513, 1, 8192) == 0
+        assert wd.attn_plan(32, 16, 32, 8, 128, 513, 32 * 513, 1, 8192)[0] == 1
+        wd.wedlm_set_attn_tail(5)
+        assert wd.attn_tail(8, 16, 32, 8, 128, 8, 64, 1, 100) == 5             # forced below half the CUs
+        assert wd.attn_tail(3, 16, 32, 8, 128, 8, 24, 1, 100) == 3             # at most B
+        assert wd.attn_tail(8, 16, 32, 8, 128, 8, 64, 0, 100) == 0             # still bf16 only
+        assert wd.attn_tail(8, 16, 32, 8, 128, 513, 8 * 513, 1, 8192) == 0     # the plan has 4 splits
+        with pytest.raises(wd.WedlmError):
+            wd.wedlm_set_attn_tail(-2)
+    finally:
+        wd.wedlm_set_attn_tail(-1)
 
 
 def test_split_override_validation():

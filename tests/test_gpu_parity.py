@@ -274,6 +274,44 @@ def test_edge_cases(label, over, split, dev):
         wd.wedlm_set_attn_split_keys(0)
 
 
+# Tail splits: a one-split plan whose longest sequences get a second
+# work-group for the back half of their keys (ranked on the device, ties
+# by index).  (label, overrides, sequences cut)
+TAIL = [
+    ("tail1_B64", dict(B=64, W=16, Hq=16, Hkv=4, L=0, L_range=(0, 3000), n_obs=None), 1),
+    ("tail16_B64", dict(B=64, W=16, Hq=16, Hkv=4, L=0, L_range=(0, 3000), n_obs=None), 16),
+    ("tail_all_ties_B64", dict(B=64, W=16, Hq=16, Hkv=4, L=0, L_range=(1000, 1002), n_obs=None), 64),
+    ("tail_empty_halves_B64", dict(B=64, W=16, Hq=16, Hkv=4, L=0, L_range=(0, 40), n_obs=None), 32),
+    ("tail8_D64_B32", dict(B=32, W=16, Hq=32, Hkv=8, D=64, L=0, L_range=(10, 2000), n_obs=None), 8),
+    ("tail16_W1_B64", dict(B=64, W=1, Hq=32, Hkv=4, L=0, L_range=(0, 1500), n_obs=None), 16),
+]
+
+
+@pytest.mark.parametrize("label,over,tail", TAIL, ids=[x[0] for x in TAIL])
+def test_tail_splits(label, over, tail, dev):
+    cfg = _cfg("ragged_b32", name=label, **over)
+    print(f"[tail] {label}: {tail} sequences cut", flush=True)
+    wd.wedlm_set_attn_tail(tail)
+    try:
+        err, status = _attn_alone(cfg, dev)
+        print(f"[tail] {label}: attention err {err:.3e}")
+        assert status == 0
+        assert err <= ATTN_TOL[cfg.dtype], err
+        inp = wl.make_attn_inputs(cfg)
+        t = wl.device_attn_inputs(inp, dev)
+        mx = int(inp.ctx_len.max())
+        assert wd.wedlm_attn_tail(t["q_phys"], t["k_cache"], t["block_table"], mx) == tail
+        run_reorder(t, cfg)
+        run_attn(t, mx)
+        torch.cuda.synchronize()
+        assert t["status"].item() == 0
+        ref = oracle.decode_step_attention(inp)
+        err2 = rel_err(wl.torch_storage_to_f64(t["out"], cfg.dtype), ref["out"])
+        assert err2 <= ATTN_TOL[cfg.dtype], err2
+    finally:
+        wd.wedlm_set_attn_tail(-1)
+
+
 def _random_shapes(n, seed):
     """Seeded draws over the shapes the entry points accept: batch, window
     (1..64), head grouping (G = 1..8), head dim, dtype, ragged prefixes
@@ -341,7 +379,17 @@ def test_split_count_does_not_change_result(dev):
         assert rel_err(o, outs[0]) <= 1e-2
 
 
-def test_device_status_bad_ctx_and_page(dev):
+@pytest.mark.parametrize("tail", [-1, 2])
+def test_device_status_bad_ctx_and_page(tail, dev):
+    # tail = 2: the two longest sequences cut in two; the skipped one ranks last
+    wd.wedlm_set_attn_tail(tail)
+    try:
+        _status_bad_ctx_and_page(dev)
+    finally:
+        wd.wedlm_set_attn_tail(-1)
+
+
+def _status_bad_ctx_and_page(dev):
     cfg = _cfg("qwen3_l2048", B=3, L=50, n_obs=4)
     inp = wl.make_attn_inputs(cfg)
     t = wl.device_attn_inputs(inp, dev)
