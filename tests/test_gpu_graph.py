@@ -26,8 +26,8 @@ from parity_checks import rounding_exact
 pytestmark = pytest.mark.gpu
 
 
-def _decode_setup(dev, steps=3, V=4096, fused=False):
-    cfg = wl.CONFIGS["qwen3_l2048"]
+def _decode_setup(dev, steps=3, V=4096, fused=False, cfg=None):
+    cfg = cfg or wl.CONFIGS["qwen3_l2048"]
     scfg = wl.SelectConfig("graph", B=cfg.B, W=cfg.W, V=V, seed=77, alpha=0.25, tau=6.0, steps=0,
                            kind="mixture")
     inp = wl.make_attn_inputs(cfg, spare_tokens=(steps + 1) * cfg.W)
@@ -263,3 +263,35 @@ def test_native_capture_of_model_steps(dev):
     _replays_match(g.launch, restore, snapshot, ref, dev)
     g.close()
     assert status.item() == 0
+
+
+def test_tail_split_steps_match_oracle_and_replay(dev):
+    # a ragged batch whose attention plan cuts its 12 longest sequences in
+    # two: the cut set is ranked on the device from ctx_len at every step,
+    # so replays of captured steps follow the contexts the steps grow
+    base = wl.CONFIGS["ragged_b32"]
+    d = {f: getattr(base, f) for f in base.__dataclass_fields__}
+    d.update(name="ragged_tail_graph", L_range=(100, 1500), seed=4242)
+    cfg = wl.AttnConfig(**d)
+    print("[graph] ragged B=32 x3 fused steps with 12 tail splits, V=4096, native capture", flush=True)
+    wd.wedlm_set_attn_tail(12)
+    try:
+        t, run, restore, snapshot, n_commit, check_oracle = _decode_setup(dev, fused=True, cfg=cfg)
+        assert wd.wedlm_attn_tail(t["q_phys"], t["k_cache"], t["block_table"],
+                                  int(t["ctx_len"].max().item()) + 4 * cfg.W) == 12
+        run()
+        torch.cuda.synchronize()
+        ref = snapshot()
+        assert int(n_commit.sum().item()) > 0
+        check_oracle(ref)
+        restore()
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        with wd.capture(cap) as g:
+            run()
+        assert g.nodes() == (9, 0), g.nodes()
+        _replays_match(g.launch, restore, snapshot, ref, dev)
+        g.close()
+        assert t["status"].item() == 0
+    finally:
+        wd.wedlm_set_attn_tail(-1)
