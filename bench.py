@@ -198,7 +198,8 @@ def summarise_decode(r):
             "window_tokens_per_s": r["value"],
             "steps_per_s": r["steps_per_s"], "split_kv": r["config"]["split_kv"],
             "attn": {"avg_ms": a["avg_ms"], "alg_bytes_per_launch": a["alg_bytes_per_launch"],
-                     "GB_per_s": a["GB_per_s"], "frac_of_hbm_peak": r["roofline"]["frac"]},
+                     "GB_per_s": a["GB_per_s"], "frac_of_hbm_peak": a["frac_of_hbm_peak"]},
+            "attn_kernel_in_steps": r["attn_kernel_in_steps"],
             "select_commit": r["select_commit"], "P_c": r["P_c"],
             "dtype": r["dtype"]}
 
@@ -337,14 +338,40 @@ def decode_leg(args, workload, with_cpu):
     other_elapsed = other_eager if other_replay is None else other_replay
     cnt = counters.cpu().numpy()
 
-    # ---- timed region 2: the attention call alone, K launches back to back on
-    # the stream it runs on (the state the stream ended in), bracketed by one
-    # pair of HIP events on that stream: its mean launch duration for the
-    # roofline.  Untimed launches of the same call come first, in rounds of
-    # ATTN_SETTLE for ATTN_SETTLE_S seconds.
-    # (An event pair around every single call inside the steps would add
-    # about 8 us of marker overhead to each measured call.)
+    # ---- the dominant kernel inside the steps: the same K steps again from
+    # the same state, launched one by one as wedlm_decode_step, each step's
+    # attention kernel carrying start / stop events taken from its own
+    # dispatch (no marker packet between the step's launches).  Its mean
+    # duration is the roofline's launch duration; the pass ends in the state
+    # the timed steps left (same steps, same bytes).
     stream = torch.cuda.current_stream()
+    Kst = args.steps
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(Kst)]
+    for e0, e1 in kev:          # create the event handles
+        e0.record(stream)
+        e1.record(stream)
+    ctx_hist = torch.empty((Kst, B), dtype=torch.int32, device=dev)
+    restart()
+    for j, i in enumerate(range(args.warmup, total_steps)):
+        ctx_hist[j].copy_(ctx)
+        wd.wedlm_decode_step(filled, pos, t["q"], t["k"], t["v"], t["q_phys"], t["k_cache"], t["v_cache"],
+                             t["block_table"], ctx, t["perm"], t["out"], cfg.rope_base, max_ctx,
+                             logits[i % len(logits)], tok, n_commit_hist[i], committed, scfg.alpha, scfg.tau,
+                             mask_id, ws_step, argmax_out=argmax_hist[i], counters=counters,
+                             dev_status=t["status"], attn_events=kev[j])
+    torch.cuda.synchronize()
+    for x, y in zip((tok, filled, pos, ctx, counters, n_commit_hist, t["out"]), state_other):
+        if not torch.equal(x, y):
+            print("the kernel-timed steps diverged from the timed steps", file=sys.stderr)
+            sys.exit(3)
+    kern_ms_each = [e0.elapsed_time(e1) for e0, e1 in kev]
+    L_hist = ctx_hist.cpu().numpy().astype(np.int64)
+
+    # ---- timed region 2: the attention call alone (split kernel and
+    # combine), K launches back to back on the stream it runs on (the state
+    # the stream ended in), bracketed by one pair of HIP events on that
+    # stream.  Untimed launches of the same call come first, in rounds of
+    # ATTN_SETTLE for ATTN_SETTLE_S seconds.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_end = time.perf_counter() + ATTN_SETTLE_S
     while time.perf_counter() < t_end:
@@ -409,7 +436,11 @@ def decode_leg(args, workload, with_cpu):
     # algorithmic bytes of one attention launch at the final lengths: K and V
     # of every visible key read once, Q read, O written
     mean_attn_bytes = float(((L_now + W) * Hkv * D * 2 * eb).sum() + 2 * B * W * Hq * D * eb)
-    achieved = mean_attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    achieved_call = mean_attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    # the split kernel inside the steps: each step's bytes at that step's lengths
+    step_bytes = ((L_hist + W) * Hkv * D * 2 * eb).sum(axis=1) + 2 * B * W * Hq * D * eb
+    kern_ms = float(np.mean(kern_ms_each))
+    achieved = float(step_bytes.sum()) / (float(np.sum(kern_ms_each)) * 1e-3) / 1e9
     # algorithmic flops: row r of a window sees L_b + r + 1 keys; 2D for QK
     # and 2D for PV per (row, key, query head)
     attn_flops = float((4 * D * Hq * (W * L_now + W * (W + 1) // 2)).sum())
@@ -442,8 +473,15 @@ def decode_leg(args, workload, with_cpu):
                    "batch": B, "window": W, "prefix_tokens_at_start": int(ctx_start.max()),
                    "vocab": args.vocab, "split_kv": [nsplit, split_keys], "tail_splits": tail},
         "steps_per_s": round(1e3 / ms_step, 2),
+        "attn_kernel_in_steps": {"kernel": f"attn_split_{'bf16' if cfg.dtype == 'bf16' else 'f32'}",
+                                 "avg_ms": round(kern_ms, 5), "min_ms": round(float(np.min(kern_ms_each)), 5),
+                                 "max_ms": round(float(np.max(kern_ms_each)), 5),
+                                 "alg_bytes_per_launch": int(step_bytes.mean()),
+                                 "GB_per_s": round(achieved, 1),
+                                 "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4)},
         "attn": {"avg_ms": round(attn_avg_ms, 5), "alg_bytes_per_launch": int(mean_attn_bytes),
-                 "GB_per_s": round(achieved, 1), "prefix_tokens": [int(x) for x in L_now],
+                 "GB_per_s": round(achieved_call, 1), "frac_of_hbm_peak": round(achieved_call / HBM_PEAK_GBS, 4),
+                 "prefix_tokens": [int(x) for x in L_now],
                  "alg_flops_per_launch": int(attn_flops),
                  "TFLOP_per_s": round(attn_flops / (attn_avg_ms * 1e-3) / 1e12, 1),
                  "mfma_frac_of_dense_peak": round(attn_flops / (attn_avg_ms * 1e-3) / mfma_peak, 4),
@@ -461,7 +499,8 @@ def decode_leg(args, workload, with_cpu):
                                                     and int(cnt[:, 1].sum()) == K * B * W)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(workload),
-                     "kernel": "wedlm_step_attn (attn_split + attn_combine)"},
+                     "kernel": f"attn_split_{'bf16' if cfg.dtype == 'bf16' else 'f32'}, the decode step's "
+                               "attention launch, inside the timed steps (start / stop from its dispatch)"},
     }
 
     if with_cpu:
@@ -1000,7 +1039,8 @@ def attn_source_hash():
 
 
 def recorded_traffic(workload):
-    """Bytes per attention launch from the committed counter summary, or None
+    """HBM bytes per launch of the split kernel (the roofline's kernel) from
+    the committed counter summary, or None
     when the workload or the attention sources differ from the profiled
     ones (the figure belongs to that kernel build; the context grows by a
     few hundred tokens over a run, a change of well under 1 %)."""
@@ -1015,7 +1055,7 @@ def recorded_traffic(workload):
     if kv.get("workload", "").strip("` ") != workload:
         return None
     try:
-        return int(kv["traffic_bytes_per_launch"].strip("` "))
+        return int(kv["split_kernel_traffic_bytes_per_launch"].strip("` "))
     except (KeyError, ValueError):
         return None
 

@@ -104,6 +104,8 @@ def load_library():
     lib.wedlm_attn_plan.restype = C.c_int
     lib.wedlm_set_attn_split_keys.argtypes = [i32]
     lib.wedlm_set_attn_split_keys.restype = C.c_int
+    lib.wedlm_decode_step_timed.argtypes = [S, C.POINTER(WedlmStepIO), P, sz, P, P, P]
+    lib.wedlm_decode_step_timed.restype = C.c_int
     lib.wedlm_attn_tail.argtypes = [S, i32]
     lib.wedlm_attn_tail.restype = i32
     lib.wedlm_set_attn_tail.argtypes = [i32]
@@ -356,9 +358,12 @@ def decode_step_workspace_tensor(q, k_cache, block_table, max_ctx_len: int, V: i
 def wedlm_decode_step(filled, pos, q, k, v, q_phys, k_cache, v_cache, block_table, ctx_len, perm, out,
                       rope_base: float, max_ctx_len: int, logits, tok, n_commit, committed, alpha: float,
                       tau: float, mask_id: int, workspace, scale: float = 0.0, argmax_out=None,
-                      entropy_out=None, counters=None, dev_status=None, stream=None):
+                      entropy_out=None, counters=None, dev_status=None, stream=None, attn_events=None):
     """One whole decode step: the arguments of wedlm_reorder, wedlm_step_attn and
-    wedlm_select_commit (same names), run as one call with fewer launches."""
+    wedlm_select_commit (same names), run as one call with fewer launches.
+    attn_events: optional (start, stop) torch.cuda.Event pair (timing enabled,
+    already recorded once so that they exist) that the attention kernel's
+    dispatch sets (wedlm_decode_step_timed)."""
     import torch
     s = _shape_from(q, k_cache, block_table)
     B, W, Hq, Hkv, D = s.B, s.W, s.Hq, s.Hkv, s.D
@@ -390,8 +395,16 @@ def wedlm_decode_step(filled, pos, q, k, v, q_phys, k_cache, v_cache, block_tabl
                      _ptr(n_commit), _ptr(committed), _ptr(argmax_out), _ptr(entropy_out), _ptr(counters),
                      _ptr(dev_status), int(V), int(max_ctx_len), int(mask_id), float(scale), float(alpha),
                      float(tau), float(rope_base))
-    _check(load_library().wedlm_decode_step(C.byref(s), C.byref(io), _ptr(workspace),
-                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+    nbytes = workspace.numel() * workspace.element_size()
+    if attn_events is None:
+        _check(load_library().wedlm_decode_step(C.byref(s), C.byref(io), _ptr(workspace), nbytes, _stream(stream)))
+    else:
+        e0, e1 = attn_events
+        h0, h1 = int(e0.cuda_event), int(e1.cuda_event)
+        if not h0 or not h1:
+            raise WedlmError("attn_events must be recorded once before use (the handles are created lazily)")
+        _check(load_library().wedlm_decode_step_timed(C.byref(s), C.byref(io), _ptr(workspace), nbytes,
+                                                      _stream(stream), C.c_void_p(h0), C.c_void_p(h1)))
 
 
 def wedlm_lmhead_select_commit_workspace(B: int, W: int, V: int, Dm: int) -> int:

@@ -753,8 +753,24 @@ extern "C" size_t wedlm_decode_step_workspace(const wedlm_shape* s, int32_t max_
     return sel ? step_attn_bytes(s, max_ctx_len) + sel : 0;
 }
 
+static int decode_step(const wedlm_shape* s, const wedlm_step_io* io, void* workspace, size_t ws_bytes,
+                       void* stream, const LaunchTiming* tm);
+
 extern "C" int wedlm_decode_step(const wedlm_shape* s, const wedlm_step_io* io, void* workspace, size_t ws_bytes,
                                  void* stream) {
+    return decode_step(s, io, workspace, ws_bytes, stream, nullptr);
+}
+
+extern "C" int wedlm_decode_step_timed(const wedlm_shape* s, const wedlm_step_io* io, void* workspace,
+                                       size_t ws_bytes, void* stream, void* attn_start, void* attn_stop) {
+    LaunchTiming tm;
+    tm.start = static_cast<hipEvent_t>(attn_start);
+    tm.stop = static_cast<hipEvent_t>(attn_stop);
+    return decode_step(s, io, workspace, ws_bytes, stream, (attn_start || attn_stop) ? &tm : nullptr);
+}
+
+static int decode_step(const wedlm_shape* s, const wedlm_step_io* io, void* workspace, size_t ws_bytes,
+                       void* stream, const LaunchTiming* tm) {
     if (!io) return fail(WEDLM_ERR_ARG, "wedlm_decode_step: io is NULL");
     int rc = check_shape(s);
     if (rc) return rc;
@@ -790,7 +806,8 @@ extern "C" int wedlm_decode_step(const wedlm_shape* s, const wedlm_step_io* io, 
         return fail(WEDLM_ERR_SHAPE, "wedlm_decode_step: grid too large (B=%d W=%d parts=%d)", s->B, s->W, sa.nparts);
     hipStream_t st = (hipStream_t)stream;
     if ((rc = hip_status(launch_step_front(ra, sa, s->dtype, st), "wedlm_decode_step front launch"))) return rc;
-    if ((rc = hip_status(launch_attn_split(aa, s->dtype, s->D, p.nw, st), "wedlm_decode_step attention launch")))
+    if ((rc = hip_status(launch_attn_split(aa, s->dtype, s->D, p.nw, st, tm),
+                         "wedlm_decode_step attention launch")))
         return rc;
     return hip_status(launch_step_back(aa, sa, s->dtype, s->D, st), "wedlm_decode_step back launch");
 }

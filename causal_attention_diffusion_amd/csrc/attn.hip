@@ -415,22 +415,29 @@ static hipError_t launch_step_back_t(const AttnArgs& a, const SelectArgs& s, hip
 }
 
 template <int D, int NW>
-static hipError_t launch_f32_t(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_f32_t(const AttnArgs& a, hipStream_t st, const LaunchTiming* tm) {
     const int npid = a.B * a.Hkv * a.row_tiles;
-    hipLaunchKernelGGL((attn_split_f32<D, NW>), dim3((unsigned)npid * a.nsplit), dim3(64 * NW), 0, st, a);
+    if (tm)
+        hipExtLaunchKernelGGL((attn_split_f32<D, NW>), dim3((unsigned)npid * a.nsplit), dim3(64 * NW), 0, st,
+                              tm->start, tm->stop, 0, a);
+    else
+        hipLaunchKernelGGL((attn_split_f32<D, NW>), dim3((unsigned)npid * a.nsplit), dim3(64 * NW), 0, st, a);
     return hipGetLastError();
 }
 
 int attn_chunk(int dtype, int nw) { return dtype == WEDLM_BF16 ? 64 : 32; }
 
-hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st);
+hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st, const LaunchTiming* tm);
 
-hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {
+hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st, const LaunchTiming* tm) {
     if (dtype == WEDLM_F32) {
-        if (D == 64) return nw == 1 ? launch_f32_t<64, 1>(a, st) : nw == 2 ? launch_f32_t<64, 2>(a, st) : launch_f32_t<64, 4>(a, st);
-        return nw == 1 ? launch_f32_t<128, 1>(a, st) : nw == 2 ? launch_f32_t<128, 2>(a, st) : launch_f32_t<128, 4>(a, st);
+        if (D == 64)
+            return nw == 1 ? launch_f32_t<64, 1>(a, st, tm) : nw == 2 ? launch_f32_t<64, 2>(a, st, tm)
+                                                             : launch_f32_t<64, 4>(a, st, tm);
+        return nw == 1 ? launch_f32_t<128, 1>(a, st, tm) : nw == 2 ? launch_f32_t<128, 2>(a, st, tm)
+                                                          : launch_f32_t<128, 4>(a, st, tm);
     }
-    return launch_attn_bf16_split(a, D, nw, st);
+    return launch_attn_bf16_split(a, D, nw, st, tm);
 }
 
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t st) {

@@ -738,20 +738,24 @@ static unsigned bf16_split_grid(const AttnArgs& a) {
 }
 
 template <int D, int NRG>
-static hipError_t launch_bf16_t(const AttnArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((attn_split_bf16<D, NRG>), dim3(bf16_split_grid(a)), dim3(512), 0, st, a);
+static hipError_t launch_bf16_t(const AttnArgs& a, hipStream_t st, const LaunchTiming* tm) {
+    if (tm)
+        hipExtLaunchKernelGGL((attn_split_bf16<D, NRG>), dim3(bf16_split_grid(a)), dim3(512), 0, st, tm->start,
+                              tm->stop, 0, a);
+    else
+        hipLaunchKernelGGL((attn_split_bf16<D, NRG>), dim3(bf16_split_grid(a)), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st) {
+hipError_t launch_attn_bf16_split(const AttnArgs& a, int D, int nrg, hipStream_t st, const LaunchTiming* tm) {
     if (D == 64) {
-        if (nrg == 1) return launch_bf16_t<64, 1>(a, st);
-        if (nrg == 2) return launch_bf16_t<64, 2>(a, st);
-        return launch_bf16_t<64, 4>(a, st);
+        if (nrg == 1) return launch_bf16_t<64, 1>(a, st, tm);
+        if (nrg == 2) return launch_bf16_t<64, 2>(a, st, tm);
+        return launch_bf16_t<64, 4>(a, st, tm);
     }
-    if (nrg == 1) return launch_bf16_t<128, 1>(a, st);
-    if (nrg == 2) return launch_bf16_t<128, 2>(a, st);
-    return launch_bf16_t<128, 4>(a, st);
+    if (nrg == 1) return launch_bf16_t<128, 1>(a, st, tm);
+    if (nrg == 2) return launch_bf16_t<128, 2>(a, st, tm);
+    return launch_bf16_t<128, 4>(a, st, tm);
 }
 
 }  // namespace wedlm

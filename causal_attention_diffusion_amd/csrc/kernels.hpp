@@ -114,9 +114,17 @@ __device__ __forceinline__ int split_len(int T_len, int nsplit, int split_keys, 
 hipError_t launch_reorder(const ReorderArgs& a, int dtype, hipStream_t stream);
 // bf16 reorder whose q/k/v come from split-K partials (a.part)
 hipError_t launch_reorder_from_partials(const ReorderArgs& a, hipStream_t stream);
+// Optional start / stop events of one launch, taken from the dispatch itself
+// (hipExtLaunchKernel): the kernel's own duration, with no marker packets
+// added to the stream.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
 hipError_t launch_attn(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
 // the split kernel alone (no combine)
-hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream);
+hipError_t launch_attn_split(const AttnArgs& a, int dtype, int D, int nw, hipStream_t stream,
+                             const LaunchTiming* tm = nullptr);
 int attn_chunk(int dtype, int nw);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 struct ModelRowArgs {

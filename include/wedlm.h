@@ -460,6 +460,18 @@ int wedlm_decode_step(const wedlm_shape *s, const wedlm_step_io *io, void *works
                       void *stream);
 
 /*
+ * wedlm_decode_step_timed -- wedlm_decode_step whose attention launch (the
+ * split kernel, the step's dominant kernel) also sets two caller-created
+ * hipEvent_t: attn_start when the kernel starts and attn_stop when it ends,
+ * both from the dispatch's own timestamps (hipExtLaunchKernel), so no
+ * marker is added to the stream and hipEventElapsedTime gives the kernel's
+ * duration.  Either may be NULL.  For profiling a running decode loop; the
+ * results are those of wedlm_decode_step.  Not for use under graph capture.
+ */
+int wedlm_decode_step_timed(const wedlm_shape *s, const wedlm_step_io *io, void *workspace, size_t ws_bytes,
+                            void *stream, void *attn_start, void *attn_stop);
+
+/*
  * wedlm_attn_plan -- the split-KV launch plan wedlm_step_attn uses for
  * this shape and bound: work-groups per (sequence, KV head, row tile)
  * (*nsplit) and keys per work-group (*split_keys).  Either may be NULL.

@@ -202,3 +202,41 @@ def test_fused_step_rejects_bad_arguments(dev):
     torch.cuda.synchronize()
     for x, y in zip((t["k_cache"], t["ctx_len"], tok), before):
         assert torch.equal(x, y)   # nothing was enqueued
+
+
+def test_timed_step_equals_plain_step(dev):
+    # wedlm_decode_step_timed: the same bytes as wedlm_decode_step, and the
+    # attention kernel's dispatch sets the two events (a positive duration
+    # shorter than the whole step)
+    cfg = wl.CONFIGS["qwen3_l2048"]
+    V, steps = 4096, 3
+    inp = wl.make_attn_inputs(cfg, spare_tokens=(steps + 1) * cfg.W)
+    max_ctx = int(inp.ctx_len.max()) + (steps + 1) * cfg.W
+    scfg = wl.SelectConfig("timed", B=cfg.B, W=cfg.W, V=V, seed=cfg.seed + 9, alpha=0.25,
+                           tau=float(np.log(V) * 0.7), steps=0, kind="mixture")
+    logits = [wl.make_logits_torch(scfg, i, dev) for i in range(steps)]
+    a = _Stream(inp, dev, V, steps, max_ctx)
+    f = _Stream(inp, dev, V, steps, max_ctx)
+    ws_a = wd.decode_step_workspace_tensor(a.t["q"], a.t["k_cache"], a.t["block_table"], max_ctx, V)
+    ws_f = wd.decode_step_workspace_tensor(f.t["q"], f.t["k_cache"], f.t["block_table"], max_ctx, V)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        e1.record(stream)
+    for i in range(steps):
+        for s_, ws, ev in ((a, ws_a, None), (f, ws_f, evs[i])):
+            u = s_.t
+            wd.wedlm_decode_step(u["filled"], u["pos"], u["q"], u["k"], u["v"], u["q_phys"], u["k_cache"],
+                                 u["v_cache"], u["block_table"], u["ctx_len"], u["perm"], s_.outs[i],
+                                 cfg.rope_base, max_ctx, logits[i], s_.tok, s_.n_commit[i], s_.committed[i],
+                                 scfg.alpha, scfg.tau, V, ws, argmax_out=s_.argmax[i], entropy_out=s_.entropy[i],
+                                 counters=s_.counters, dev_status=u["status"], attn_events=ev)
+            s_.keep(i)
+    torch.cuda.synchronize()
+    ra, rf = a.result(), f.result()
+    for name in ra:
+        assert torch.equal(ra[name], rf[name]), f"timed step: {name} differs"
+    ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    print(f"[step] timed attention kernel: {[round(x * 1e3, 1) for x in ms]} us", flush=True)
+    assert all(0.0 < x < 5.0 for x in ms), ms
