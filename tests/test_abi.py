@@ -127,6 +127,12 @@ def test_decode_step_validation_and_workspace():
                       4.0, 1e6)   # no logits
     assert lib.wedlm_decode_step(C.byref(s), C.byref(nul), fake, need, None) == ERR_ARG
     assert lib.wedlm_decode_step_workspace(C.byref(s), 2000, 0) == 0
+    # the timed form checks the same arguments before it launches anything
+    assert lib.wedlm_decode_step_timed(C.byref(s), C.byref(io), fake, need - 1, None, None, None) == ERR_WS
+    assert lib.wedlm_decode_step_timed(C.byref(s), C.byref(nul), fake, need, None, fake, fake) == ERR_ARG
+    assert lib.wedlm_decode_step_timed(C.byref(s), None, fake, need, None, None, None) == ERR_ARG
+    assert lib.wedlm_attn_tail(C.byref(_shape(W=65)), 2000) == -1
+    assert lib.wedlm_attn_tail(C.byref(s), -1) == -1
     assert lib.wedlm_decode_step(C.byref(_shape(W=65)), C.byref(io), fake, need, None) == ERR_SHAPE
 
 
