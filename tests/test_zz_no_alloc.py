@@ -1,8 +1,8 @@
 """wedlm_step_attn_noalloc (split partials in the library's own device
 array, no workspace argument) against wedlm_step_attn (caller workspace),
-through the C ABI on the same inputs: two calls in a row, the second on a
-smaller input, each compared element by element with the workspace entry
-point.  Both run the same kernels and split plan, so the outputs must be
+through the C ABI on the same inputs: three calls in a row, the last on a
+much smaller input, each compared element by element with the workspace
+entry point.  Both run the same kernels and split plan, so the outputs must be
 identical bytes (the attention tolerance would be 2e-2 for bf16).  A shape
 whose partials exceed the array is refused on the host before any launch."""
 import numpy as np
@@ -41,12 +41,15 @@ def _both(t, max_ctx):
 
 
 def test_noalloc_matches_workspace_entry_point(dev):
-    # first call: long_b4 (8 splits, about 17 MB of partials in the array);
-    # second: qwen3_l2048, a smaller plan over the same array
-    for name in ("long_b4", "qwen3_l2048"):
+    # ragged_b32 (tail splits: the back parts name their sequences in the
+    # array), then long_b4 (8 splits, about 17 MB of partials in the array),
+    # then qwen3_l2048, a smaller plan over the same array
+    for name in ("ragged_b32", "long_b4", "qwen3_l2048"):
         cfg = wl.CONFIGS[name]
         print(f"[noalloc] {name}", flush=True)
         t, max_ctx = _inputs(cfg, dev)
+        tail = wd.wedlm_attn_tail(t["q_phys"], t["k_cache"], t["block_table"], max_ctx)
+        assert (tail > 0) == (name == "ragged_b32"), (name, tail)
         out_na, out_ws, ws_bytes = _both(t, max_ctx)
         assert 0 < ws_bytes <= wd.wedlm_step_attn_noalloc_limit()
         assert torch.equal(out_na.view(torch.int16), out_ws.view(torch.int16)), name
