@@ -157,16 +157,16 @@ static Plan make_plan(const wedlm_shape* s, int32_t max_ctx_len) {
     // Tail splits: a one-split bf16 plan whose (sequence, KV head) groups
     // fill at least half of the CUs in one round is bound by its longest
     // sequences, each streaming alone on one CU after the short ones are
-    // done.  The longest quarter of the sequences (ranked on the device from
-    // ctx_len) get a second work-group for the back half of their keys;
-    // those are dispatched after the first round and start on the CUs the
-    // shortest sequences free.  3/8 of the batch measured best at the
-    // ragged 32-sequence shape (a quarter, a half, three quarters within
-    // 1-2 % below it).
+    // done.  The longest 3/8 of the sequences (ranked on the device from
+    // ctx_len) get a second work-group for the back part of their keys
+    // (where the cut falls: tail_cut); those are dispatched after the first
+    // round and start on the CUs the shortest sequences free.  3/8 of the
+    // batch measured best at the ragged 32-sequence shape (a quarter, a
+    // half, three quarters 1-4 % slower).
     p.tail = 0;
     {
         const int32_t ov = g_tail_override.load(std::memory_order_relaxed);
-        const int64_t cus = device_cus();
+        const int64_t cus = p.cus;
         const bool fits = s->dtype == WEDLM_BF16 && p.nsplit == 1 && p.row_tiles == 1 && s->B >= 2 &&
                           s->B <= kMaxSplitPages / 2 && pairs <= cus;
         if (fits && ov > 0) p.tail = ov < s->B ? ov : s->B;

@@ -295,7 +295,7 @@ __device__ __forceinline__ void combine_rows(const AttnArgs& a, int blk, int tid
     int pid, m_loc, rt, kvh, b;
     if (a.tail > 0) {
         // tail plan: only the sequences cut in two have partials to merge;
-        // group g is the second half's work-group, which named its sequence
+        // group g is the back part's work-group, which named its sequence
         const int g = (int)(row / a.RT);
         if (g >= a.tail * a.Hkv) return;
         m_loc = (int)(row - (long)g * a.RT);

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(512) void attn_split_bf16(AttnArgs a) {
         cut = second || s_tail_cut;
         bk = tb * a.Hkv + kv;
         if (cut) {
-            // back half j = rank * Hkv + head starts at once (j < tail_free)
+            // back part j = rank * Hkv + head starts at once (j < tail_free)
             // or after the first round of the (j - tail_free) / Hkv-th
             // shortest sequence
             const int j = (second ? e : s_tail_rank) * a.Hkv + kv;

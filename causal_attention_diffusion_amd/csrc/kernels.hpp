@@ -49,20 +49,21 @@ struct AttnArgs {
     // Tail splits (bf16, one row tile, nsplit == 2; 0 = off): ids [0, B*Hkv)
     // run the first split of every (sequence, KV head) -- the whole sequence
     // unless it is one of the `tail` longest, which are cut in two -- and
-    // ids past them the second halves, longest sequence first.  tail_seq
-    // [tail * Hkv] receives the sequence of each second half (for the
+    // ids past them the back parts, longest sequence first.  tail_seq
+    // [tail * Hkv] receives the sequence of each back part (for the
     // combine, which merges only those).
     int tail;
-    int tail_free;      // CUs without a first-round work-group (their second halves start at once)
+    int tail_free;      // CUs without a first-round work-group (back parts that start at once)
     int32_t* tail_seq;
 };
 
-// First key of the back half of a sequence with T_len keys cut in two by the
-// tail plan.  The back half's work-group starts when a CU frees up: at once
+// First key of the back part of a sequence with T_len keys cut in two by the
+// tail plan.  The back part's work-group starts when a CU frees up: at once
 // for the first tail_free of them, else when the first-round work-groups of
 // a short sequence finish (start_keys: that sequence's keys, a stand-in for
-// its time).  Both halves then end together when the front half takes
-// (T_len + start_keys) / 2 keys, rounded up to the ring stage, at most T_len.
+// its time).  Both parts would end together at one streaming rate when the
+// front part takes (T_len + start_keys) / 2 keys, rounded up to the ring
+// stage, at most T_len.
 __device__ __forceinline__ int tail_cut(int T_len, int start_keys, int align) {
     const int h = ((T_len + start_keys + 1) / 2 + align - 1) / align * align;
     return h < T_len ? h : T_len;
